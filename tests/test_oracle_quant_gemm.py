@@ -1,0 +1,85 @@
+"""Pins for oracle.quant, oracle.gemm and oracle.bf16 (CPU only)."""
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import synth
+from oracle import bf16, gemm, quant
+
+
+def _torch_bf16_bits(x32):
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch_including_ties():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(100_000).astype(np.float32) * np.float32(3.0)
+    # exact ties: upper half odd/even with lower half 0x8000
+    ties = (np.arange(0, 4096, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    for arr in (x, ties, np.array([0.0, -0.0, 1e-40, -3.5e38], dtype=np.float32)):
+        assert (bf16.round_f32(arr) == _torch_bf16_bits(arr)).all()
+    bits = synth.normal_bf16((1000,), 1.0, 5)
+    assert (bf16.round_f32(bf16.to_f32(bits)) == bits).all()   # exact round trip
+
+
+def test_quant_extremes_ties_and_zero_rows():
+    row = np.array([[254.0, 1.0, 3.0, 5.0, -1.0, -3.0, -254.0, 0.0]], dtype=np.float32)
+    q, s = quant.quantize(row)
+    # x*127/254 = x/2: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2 (ties to even); +-absmax -> +-127
+    assert q.tolist() == [[127, 0, 2, 2, 0, -2, -127, 0]]
+    assert s[0] == np.float32(254.0) / np.float32(127.0) == np.float32(2.0)
+    q, s = quant.quantize(np.zeros((3, 16), dtype=np.float32))
+    assert (q == 0).all() and (s == 0).all()
+
+
+def test_quant_matches_exact_rational_rounding_and_error_bound():
+    x = bf16.to_f32(synth.normal_bf16((2000, 128), 0.5, 6))
+    q, s = quant.quantize(x)
+    xh = quant.dequantize(q, s)
+    a = np.abs(x).max(axis=1)
+    assert (np.abs(q).max(axis=1) == 127).all()          # the absmax element maps to +-127
+    # |x - x_hat| <= scale/2 plus float32 rounding of q*scale and of scale itself
+    err = np.abs(x - xh)
+    bound = s[:, None] * np.float32(0.5) + np.abs(xh) * np.float32(2.0 ** -23) + s[:, None] * np.float32(127 * 2.0 ** -24)
+    assert (err <= bound).all()
+    # every code equals round-half-even of the correctly rounded binary32 quotient
+    for r in range(0, 2000, 97):
+        ar = Fraction(float(a[r]))
+        for d in range(0, 128, 7):
+            exact = Fraction(float(x[r, d])) * 127 / ar
+            quot = np.float32(float(exact))          # nearest binary32 (double rounding is exact here)
+            fl = int(np.floor(quot))
+            frac = Fraction(float(quot)) - fl
+            want = fl + (1 if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2) else 0)
+            assert q[r, d] == max(-127, min(127, want))
+    assert s[5] == np.float32(Fraction(float(a[5])) / 127)
+
+
+def test_projection_identity_is_bit_exact():
+    h = synth.normal_bf16((37, 64), 1.0, 7)
+    eye = bf16.round_f32(np.eye(64, dtype=np.float32))
+    assert (gemm.project_bf16(h, eye) == h).all()
+
+
+def test_projection_small_integers_exact():
+    rng = np.random.default_rng(2)
+    hi = rng.integers(-8, 9, size=(50, 96))
+    wi = rng.integers(-8, 9, size=(40, 96))
+    h = bf16.round_f32(hi.astype(np.float32))
+    w = bf16.round_f32(wi.astype(np.float32))
+    exact = hi.astype(np.int64) @ wi.astype(np.int64).T                 # |sum| < 2^24: exact in fp32
+    assert (gemm.project_f32(h, w) == exact.astype(np.float32)).all()
+    assert (gemm.project_bf16(h, w) == _torch_bf16_bits(exact.astype(np.float32))).all()
+
+
+def test_projection_random_within_one_bf16_ulp_of_float64():
+    h = synth.normal_bf16((64, 1536), 1.0, 8)
+    w = synth.normal_bf16((32, 1536), (1 / 1536) ** 0.5, 9)
+    ref = bf16.to_f64(h) @ bf16.to_f64(w).T
+    got = bf16.to_f64(gemm.project_bf16(h, w))
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert (np.abs(got - ref) <= ulp).all()

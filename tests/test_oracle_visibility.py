@@ -1,0 +1,109 @@
+"""Pins for oracle.visibility and oracle.ring (CPU only).
+
+Each check compares the oracle with something other than itself: a closed
+form, a queue simulation of "keep the sink, evict the oldest", the page's
+worked example, or the independent slot model.
+"""
+
+import os
+from collections import deque
+
+import pytest
+
+from oracle import ring, visibility
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _queue_visible(f0, C, S, W):
+    """Generate frames one at a time keeping sink frames forever and a FIFO
+    of at most W other frames (the oldest leaves first)."""
+    sink, fifo = [], deque()
+    for f in range(f0):
+        if f < S:
+            sink.append(f)
+        else:
+            fifo.append(f)
+            while len(fifo) > W:
+                fifo.popleft()
+    # frames below S may also be among the "last W" frames; the union counts them once
+    last_w = set(range(max(0, f0 - W), f0))
+    return sorted(set(sink) | set(fifo) | last_w | set(range(f0, f0 + C)))
+
+
+@pytest.mark.parametrize("S", range(0, 5))
+@pytest.mark.parametrize("W", [0, 1, 2, 3, 5, 6, 9, 12, 21, 25])
+@pytest.mark.parametrize("C", [1, 2, 3, 4])
+def test_visible_set_closed_form_and_queue(S, W, C):
+    for f0 in range(0, 200, 1 if W < 10 else 3):
+        v = visibility.visible_frames(f0, C, S, W)
+        assert len(v) == min(f0, S + W) + C, (f0, C, S, W)
+        assert v == _queue_visible(f0, C, S, W)
+        # the own chunk is always visible, nothing later is
+        assert all(f in v for f in range(f0, f0 + C))
+        assert max(v) == f0 + C - 1 if v else True
+
+
+@pytest.mark.parametrize("S", range(0, 5))
+@pytest.mark.parametrize("W", [0, 1, 2, 5, 6, 12, 21])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 13, 30])
+def test_ring_model_holds_exactly_the_cached_visible_set(S, W, n):
+    if S + W == 0:
+        pytest.skip("no slots")
+    r = ring.RingModel(S, W)
+    for _ in range(25):
+        r.append(n)
+        assert r.occupied_frames() == visibility.cached_visible_frames(r.f0, S, W)
+        # one frame per slot, and every occupied slot is where slot_of puts it
+        for s, f in enumerate(r.slot_frame):
+            if f >= 0:
+                assert r.slot_of(f) == s
+        assert r.retained_frames() == visibility.cached_visible_frames(r.f0, S, W)
+
+
+def test_ring_recache_rewrites_every_retained_slot():
+    r = ring.RingModel(3, 12)
+    for _ in range(10):
+        r.append(3, src_of_frame=lambda f: ("append", f))
+    frames = r.retained_frames()
+    assert len(frames) == 15
+    r.recache(15, src_of_block=lambda idx: ("recache", idx))
+    for s, f in enumerate(r.slot_frame):
+        assert r.slot_src[s][0] == "recache"
+        assert frames[r.slot_src[s][1]] == f
+    with pytest.raises(ValueError):
+        r.recache(14)
+
+
+def _read_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def test_golden_autoregressive_mask_example():
+    # one latent frame per chunk z_i, no sink, window holding the whole history
+    for q, vis, invis in _read_rows("ar_mask_example.txt"):
+        q = int(q)
+        v = visibility.visible_frames(q, 1, 0, 1000)
+        assert v == [int(x) for x in vis.split(",")]
+        for x in invis.split(","):
+            assert int(x) not in v
+
+
+def test_golden_attention_config_sink_and_window():
+    ((C, W, S),) = [tuple(int(x) for x in r) for r in _read_rows("attention_config_example.txt")]
+    for k in range(0, 60):
+        f0 = k * C
+        v = visibility.visible_frames(f0, C, S, W)
+        if f0 >= S:
+            # the first S frames stay visible however long the video gets
+            assert all(f in v for f in range(S))
+        # nothing older than the window is visible apart from the sink
+        assert all(f < S or f >= f0 - W for f in v)
+        # the context stops growing: at most S + W cached frames plus the chunk
+        assert len(v) <= S + W + C
