@@ -1,0 +1,186 @@
+/*
+ * ll_cache.h -- C ABI of the MI355X (gfx950) streaming sink+window KV-cache library.
+ *
+ * What the library computes (sources are cited per entry point):
+ *   [LL-dpshk]  "LongLive: Real-time Interactive Long Video Generation" explainer,
+ *               dpshk.com: §二 frame-level autoregressive generation with a KV cache,
+ *               §三 KV-recache, §五 Short Window Attention, §六 Frame Sink.
+ *   [LL-tw]     "英伟达突破视频生成瓶颈：LONGLIVE让普通电脑也能实时生成超长视频",
+ *               techwalker.com: §四 short window + frame sink, §六 chunk of 3 latent
+ *               frames, window of 9, first 3 frames as sink, recache scope.
+ *   [LL2-wmrh]  "LongLive-2.0: An NVFP4 Parallel Infrastructure for Long Video
+ *               Generation" explainer, wmrh.cn: §6 autoregressive mask, §15.2-§15.3
+ *               low-precision KV cache and its dequantisation.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers on the device that was current when the
+ *     cache was created, 16-byte aligned, and owned by the caller.  They must stay
+ *     valid until the enqueued work has run (the library keeps no reference).
+ *   - Token tensors are row-major [tokens][heads][head_dim] bf16 (IEEE binary32
+ *     upper halves), contiguous.  "A frame" is tokens_per_frame consecutive tokens.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     device work of a call is enqueued on it; nothing blocks the host.
+ *   - Host-side bookkeeping (frames seen f0, which frame each slot holds) is
+ *     updated when a call is enqueued, so calls on one cache must be issued in
+ *     stream order and must not race from several host threads.
+ *   - Every function returns a status; no exception or abort crosses the ABI.
+ *     Arguments are validated BEFORE any HIP call: LL_ERR_INVALID for bad
+ *     arguments, LL_ERR_STATE for calls the cache's state forbids, LL_ERR_OOM when
+ *     device memory cannot be allocated, LL_ERR_HIP when the HIP runtime reports
+ *     an error (no device, launch failure).  ll_last_error() gives text for the
+ *     last failure on the calling thread.  Device faults of enqueued work are
+ *     reported by the HIP runtime at a later synchronisation.
+ */
+#ifndef LL_CACHE_H
+#define LL_CACHE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ll_cache ll_cache; /* opaque; owns its slot memory */
+
+typedef enum { LL_KV_BF16 = 0, LL_KV_INT8 = 1 } ll_kv_dtype;
+
+typedef enum {
+  LL_OK = 0,
+  LL_ERR_INVALID = 1,
+  LL_ERR_OOM = 2,
+  LL_ERR_STATE = 3,
+  LL_ERR_HIP = 4
+} ll_status;
+
+/* Largest S + W the library accepts (slots per layer). */
+#define LL_MAX_SLOTS 128
+
+/*
+ * ll_cache_create -- allocate the per-layer KV cache of the sink + window policy.
+ * [LL-dpshk §六]: the cache holds the sink frames' K/V permanently plus the K/V of
+ * the most recent window; [LL-dpshk §五]: older K/V are evicted, so memory stays
+ * bounded; [LL-tw §六]: sink = first 3 latent frames, window = 9 latent frames.
+ *
+ *   layers            >= 1
+ *   heads             >= 1
+ *   head_dim          64 or 128
+ *   tokens_per_frame  >= 1 (T)
+ *   sink_frames       S >= 0
+ *   window_frames     W >= 0, 1 <= S + W <= LL_MAX_SLOTS
+ *   kv_dtype          LL_KV_BF16: cached K/V stored as bf16 (bit copies of the input)
+ *                     LL_KV_INT8: cached K/V stored as int8 codes with one fp32 scale
+ *                     per (token, head) row:  scale = absmax/127,
+ *                     q = clamp(rint((x*127)/absmax), -127, 127), 0 for an all-zero row
+ *   out               receives the handle
+ *
+ * Device memory: layers * 2 * (S+W) * T * heads * head_dim * (2 or 1) bytes, plus
+ * layers * 2 * (S+W) * T * heads * 4 bytes of scales for int8.  Slot contents start
+ * undefined; no slot is visible until written.  Errors: LL_ERR_INVALID, LL_ERR_OOM,
+ * LL_ERR_HIP.
+ */
+ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_frame,
+                          int sink_frames, int window_frames, int kv_dtype,
+                          ll_cache **out);
+
+/* Free the cache's device memory and the handle (NULL is accepted).  The caller
+ * must make sure no enqueued work still uses it. */
+void ll_cache_destroy(ll_cache *c);
+
+/*
+ * ll_cache_append -- the append/evict step after a chunk is finished.
+ * [LL-dpshk §二]: after a chunk is generated its K/V enter the cache and are reused;
+ * [LL-dpshk §五]: K/V older than the window are evicted; [LL-dpshk §六]: sink frames
+ * stay.  Frames f0 .. f0+n_frames-1 of `layer` are written (frame f goes to slot f
+ * if f < S, else to window slot S + (f-S) mod W, else it is dropped when W = 0; a
+ * later frame of the same call replaces an earlier one), then f0 += n_frames.
+ *   K, V       [n_frames*T][heads][head_dim] bf16 (the finished chunk's keys/values)
+ *   n_frames   >= 1
+ * Errors: LL_ERR_INVALID (layer, pointers, n_frames), LL_ERR_HIP.
+ */
+ll_status ll_cache_append(ll_cache *c, int layer, const void *K, const void *V,
+                          int n_frames, void *stream);
+
+/*
+ * ll_attn_sink_window -- attention of one chunk over sink + window + own chunk.
+ * [LL-dpshk §五, §六]; [LL-tw §四, §六]; [LL2-wmrh §6] (a chunk sees earlier chunks
+ * and itself, never a later one).  For a chunk starting at frame f0 (the layer's
+ * frames seen so far) each query token attends to every token of the frames
+ *     {f < min(S, f0)} U {max(0, f0-W) <= f < f0} U {own chunk's frames}
+ * with full visibility inside the own chunk:
+ *     out = softmax((Q K^T) / sqrt(head_dim)) V   per head, over those keys.
+ * The cache is read only (denoise passes of one chunk may call this repeatedly).
+ * For LL_KV_INT8 caches the cached keys/values are dequantised (q * scale); the own
+ * chunk is used as given.
+ *   Q, K_chunk, V_chunk   [n_frames*T][heads][head_dim] bf16 (n_frames >= 1)
+ *   out                   [n_frames*T][heads][head_dim] bf16, written completely
+ * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax statistics, bf16
+ * probabilities for the P*V product, output rounded to bf16.
+ * Errors: LL_ERR_INVALID, LL_ERR_HIP.
+ */
+ll_status ll_attn_sink_window(ll_cache *c, int layer, const void *Q, const void *K_chunk,
+                              const void *V_chunk, int n_frames, void *out, void *stream);
+
+/*
+ * ll_cache_recache -- rewrite the retained cache at a prompt switch.
+ * [LL-dpshk §三 items 3 and 5]: the recache context is the sink latents plus the
+ * recent-window latents; the old KV cache is dropped and a new one computed from
+ * them under the new prompt replaces it.  K_all/V_all hold the recomputed K/V of
+ * the retained frames in logical order -- sink frames ascending, then window
+ * frames oldest to newest -- and every retained slot is overwritten; f0 is
+ * unchanged.
+ *   K_all, V_all  [n_frames*T][heads][head_dim] bf16
+ *   n_frames      must equal min(f0, S+W) (else LL_ERR_STATE; 0 frames cached is
+ *                 LL_ERR_STATE too)
+ * Errors: LL_ERR_INVALID, LL_ERR_STATE, LL_ERR_HIP.
+ */
+ll_status ll_cache_recache(ll_cache *c, int layer, const void *K_all, const void *V_all,
+                           int n_frames, void *stream);
+
+/*
+ * ll_cache_recache_window -- recache variant that keeps the sink.
+ * [LL-tw §六]: recomputation is limited to the most recent W frames and the sink
+ * tokens stay unchanged.  K_win/V_win hold the window frames oldest to newest.
+ *   n_frames  must equal min(max(f0 - S, 0), W) and be >= 1 (else LL_ERR_STATE)
+ * Errors: LL_ERR_INVALID, LL_ERR_STATE, LL_ERR_HIP.
+ */
+ll_status ll_cache_recache_window(ll_cache *c, int layer, const void *K_win,
+                                  const void *V_win, int n_frames, void *stream);
+
+/*
+ * ll_kv_project -- recompute keys and values from hidden states (the recache
+ * projection).  [LL-dpshk §三 item 4]: K = W_K h', V = W_V h'.  Row form:
+ *     K_all = h W_K^T,  V_all = h W_V^T
+ *   h         [n_tokens][d_in] bf16
+ *   W_K, W_V  [d_out][d_in] bf16 (the matrices of the column form K = W_K h')
+ *   K_all, V_all  [n_tokens][d_out] bf16 (= [tokens][heads][head_dim] when
+ *             d_out = heads*head_dim), rounded to nearest-even from fp32 sums
+ *   n_tokens >= 1; d_in a multiple of 64; d_out a multiple of 128
+ * Errors: LL_ERR_INVALID, LL_ERR_HIP.
+ */
+ll_status ll_kv_project(const void *h, const void *W_K, const void *W_V, int n_tokens,
+                        int d_in, int d_out, void *K_all, void *V_all, void *stream);
+
+/* ---- introspection (host-side, no device work) --------------------------- */
+
+/* Frames appended to `layer` so far (f0). */
+ll_status ll_cache_frames_seen(const ll_cache *c, int layer, int64_t *f0);
+
+/* For each of the S+W slots of `layer`, the frame it holds, or -1 if empty.
+ * frame_of_slot must have room for S+W entries (host memory). */
+ll_status ll_cache_slot_frames(const ll_cache *c, int layer, int64_t *frame_of_slot);
+
+/* Device pointers of `layer`'s slot arrays (read them after synchronising):
+ *   K, V        [S+W][T][heads][head_dim], bf16 or int8 (kv_dtype)
+ *   K_scale, V_scale  [S+W][T][heads] fp32 for int8 caches, NULL for bf16
+ * Any output pointer may be NULL. */
+ll_status ll_cache_slot_view(const ll_cache *c, int layer, void **K, void **V,
+                             void **K_scale, void **V_scale);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char *ll_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LL_CACHE_H */

@@ -1,0 +1,320 @@
+// cache.cpp -- the C ABI: cache handle, host bookkeeping, validation, kernel dispatch.
+//
+// The handle owns one device allocation holding, per layer, the K and V slot arrays
+// [S+W][T][H][D] (bf16 or int8) and, for int8, their [S+W][T][H] fp32 scales.  Host
+// bookkeeping per layer: frames seen (f0) and the frame held by each slot.  Every
+// argument is checked before the first HIP call so that errors are testable on a
+// machine without a GPU.
+#include "../../include/ll_cache.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+#include "slots.h"
+
+static_assert(LL_MAX_SLOTS == ll::kMaxPlan, "plan table size must match LL_MAX_SLOTS");
+
+struct ll_cache {
+  int layers = 0, heads = 0, head_dim = 0, T = 0, S = 0, W = 0;
+  int kv_dtype = LL_KV_BF16;
+  int device = -1;
+  int64_t rows_per_frame = 0;   // T * heads
+  size_t kv_bytes = 0;          // one K (or V) slot array of one layer
+  size_t sc_bytes = 0;          // one K (or V) scale array of one layer
+  void* mem = nullptr;
+  std::vector<int64_t> f0;
+  std::vector<std::vector<int64_t>> slot_frame;
+
+  char* base() const { return static_cast<char*>(mem); }
+  void* k(int l) const { return base() + (size_t(2) * l) * kv_bytes; }
+  void* v(int l) const { return base() + (size_t(2) * l + 1) * kv_bytes; }
+  float* ks(int l) const {
+    return sc_bytes ? reinterpret_cast<float*>(base() + size_t(2) * layers * kv_bytes + (size_t(2) * l) * sc_bytes) : nullptr;
+  }
+  float* vs(int l) const {
+    return sc_bytes ? reinterpret_cast<float*>(base() + size_t(2) * layers * kv_bytes + (size_t(2) * l + 1) * sc_bytes)
+                    : nullptr;
+  }
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+ll_status fail(ll_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ll_status fail(ll_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ll_status ok() {
+  g_err.clear();
+  return LL_OK;
+}
+
+ll_status hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();  // clear the sticky launch error for the next call
+  return fail(LL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;   // token rows addressed with int arithmetic
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ll_status check_layer(const ll_cache* c, int layer) {
+  if (!c) return fail(LL_ERR_INVALID, "null cache handle");
+  if (layer < 0 || layer >= c->layers) return fail(LL_ERR_INVALID, "layer %d out of range [0, %d)", layer, c->layers);
+  return LL_OK;
+}
+
+ll_status check_tensor(const void* p, const char* name) {
+  if (!p) return fail(LL_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(p)) return fail(LL_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return LL_OK;
+}
+
+ll_status check_frames(const ll_cache* c, int n_frames) {
+  if (n_frames <= 0) return fail(LL_ERR_INVALID, "n_frames must be >= 1 (got %d)", n_frames);
+  if (int64_t(n_frames) * c->T > kMaxRows) return fail(LL_ERR_INVALID, "n_frames * tokens_per_frame too large");
+  return LL_OK;
+}
+
+ll_status check_device(const ll_cache* c) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != c->device)
+    return fail(LL_ERR_INVALID, "current device %d is not the cache's device %d", dev, c->device);
+  return LL_OK;
+}
+
+#define LL_TRY(expr)                 \
+  do {                               \
+    ll_status _s = (expr);           \
+    if (_s != LL_OK) return _s;      \
+  } while (0)
+
+ll_status write_frames(ll_cache* c, int layer, const void* K, const void* V, const std::vector<ll::WriteEntry>& plan,
+                       hipStream_t s, const char* what) {
+  ll::WriteParams wp{};
+  wp.srcK = static_cast<const uint16_t*>(K);
+  wp.srcV = static_cast<const uint16_t*>(V);
+  wp.dstK = c->k(layer);
+  wp.dstV = c->v(layer);
+  wp.dstKs = c->ks(layer);
+  wp.dstVs = c->vs(layer);
+  wp.rows_per_frame = c->rows_per_frame;
+  wp.n = int(plan.size());
+  for (size_t i = 0; i < plan.size(); ++i) {
+    wp.plan_src[i] = plan[i].src;
+    wp.plan_slot[i] = plan[i].slot;
+  }
+  hipError_t e = ll::launch_kv_write(wp, c->head_dim, c->kv_dtype == LL_KV_INT8, s);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return LL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ll_last_error(void) { return g_err.c_str(); }
+
+ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_frame, int sink_frames,
+                          int window_frames, int kv_dtype, ll_cache** out) {
+  if (!out) return fail(LL_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (layers < 1) return fail(LL_ERR_INVALID, "layers must be >= 1");
+  if (heads < 1) return fail(LL_ERR_INVALID, "heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(LL_ERR_INVALID, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (tokens_per_frame < 1) return fail(LL_ERR_INVALID, "tokens_per_frame must be >= 1");
+  if (sink_frames < 0 || window_frames < 0) return fail(LL_ERR_INVALID, "sink_frames and window_frames must be >= 0");
+  const int64_t slots = int64_t(sink_frames) + window_frames;
+  if (slots < 1 || slots > LL_MAX_SLOTS)
+    return fail(LL_ERR_INVALID, "sink_frames + window_frames must be in [1, %d]", LL_MAX_SLOTS);
+  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8) return fail(LL_ERR_INVALID, "unknown kv_dtype %d", kv_dtype);
+  const int64_t rows = int64_t(tokens_per_frame) * heads;
+  if (slots * tokens_per_frame > kMaxRows || rows > kMaxRows) return fail(LL_ERR_INVALID, "cache too large");
+  const int64_t elt = kv_dtype == LL_KV_INT8 ? 1 : 2;
+  auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+  const int64_t kv_bytes = round256(slots * rows * head_dim * elt);
+  const int64_t sc_bytes = kv_dtype == LL_KV_INT8 ? round256(slots * rows * 4) : 0;
+  const double total = double(layers) * 2.0 * double(kv_bytes + sc_bytes);
+  if (total > double(int64_t(1) << 46)) return fail(LL_ERR_INVALID, "cache too large (%.3g bytes)", total);
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* mem = nullptr;
+  e = hipMalloc(&mem, size_t(total));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(LL_ERR_OOM, "hipMalloc of %.3g bytes failed: %s", total, hipGetErrorString(e));
+  }
+  ll_cache* c = new ll_cache;
+  c->layers = layers;
+  c->heads = heads;
+  c->head_dim = head_dim;
+  c->T = tokens_per_frame;
+  c->S = sink_frames;
+  c->W = window_frames;
+  c->kv_dtype = kv_dtype;
+  c->device = dev;
+  c->rows_per_frame = rows;
+  c->kv_bytes = size_t(kv_bytes);
+  c->sc_bytes = size_t(sc_bytes);
+  c->mem = mem;
+  c->f0.assign(size_t(layers), 0);
+  c->slot_frame.assign(size_t(layers), std::vector<int64_t>(size_t(slots), -1));
+  *out = c;
+  return ok();
+}
+
+void ll_cache_destroy(ll_cache* c) {
+  if (!c) return;
+  if (c->mem) (void)hipFree(c->mem);
+  delete c;
+}
+
+ll_status ll_cache_append(ll_cache* c, int layer, const void* K, const void* V, int n_frames, void* stream) {
+  LL_TRY(check_layer(c, layer));
+  LL_TRY(check_tensor(K, "K"));
+  LL_TRY(check_tensor(V, "V"));
+  LL_TRY(check_frames(c, n_frames));
+  LL_TRY(check_device(c));
+  const int64_t f0 = c->f0[size_t(layer)];
+  const std::vector<ll::WriteEntry> plan = ll::append_plan(f0, n_frames, c->S, c->W);
+  LL_TRY(write_frames(c, layer, K, V, plan, static_cast<hipStream_t>(stream), "append launch"));
+  for (const ll::WriteEntry& w : plan) c->slot_frame[size_t(layer)][size_t(w.slot)] = w.frame;
+  c->f0[size_t(layer)] = f0 + n_frames;
+  return ok();
+}
+
+ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void* K_chunk, const void* V_chunk,
+                              int n_frames, void* out, void* stream) {
+  LL_TRY(check_layer(c, layer));
+  LL_TRY(check_tensor(Q, "Q"));
+  LL_TRY(check_tensor(K_chunk, "K_chunk"));
+  LL_TRY(check_tensor(V_chunk, "V_chunk"));
+  LL_TRY(check_tensor(out, "out"));
+  LL_TRY(check_frames(c, n_frames));
+  LL_TRY(check_device(c));
+  const int64_t n_vis = ll::cached_frames(c->f0[size_t(layer)], c->S, c->W);
+  ll::AttnParams p{};
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.Kc = static_cast<const uint16_t*>(K_chunk);
+  p.Vc = static_cast<const uint16_t*>(V_chunk);
+  p.out = static_cast<uint16_t*>(out);
+  p.cK = c->k(layer);
+  p.cV = c->v(layer);
+  p.cKs = c->ks(layer);
+  p.cVs = c->vs(layer);
+  p.nq = int(int64_t(n_frames) * c->T);
+  p.ncache = int(n_vis * c->T);
+  p.H = c->heads;
+  p.c = float(1.4426950408889634 / std::sqrt(double(c->head_dim)));
+  hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype == LL_KV_INT8, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+ll_status ll_cache_recache(ll_cache* c, int layer, const void* K_all, const void* V_all, int n_frames,
+                           void* stream) {
+  LL_TRY(check_layer(c, layer));
+  LL_TRY(check_tensor(K_all, "K_all"));
+  LL_TRY(check_tensor(V_all, "V_all"));
+  const int64_t f0 = c->f0[size_t(layer)];
+  const int64_t need = ll::cached_frames(f0, c->S, c->W);
+  if (need == 0) return fail(LL_ERR_STATE, "recache: layer %d holds no frames", layer);
+  if (n_frames != need)
+    return fail(LL_ERR_STATE, "recache: n_frames must equal min(f0, S+W) = %lld (got %d)", (long long)need, n_frames);
+  LL_TRY(check_frames(c, n_frames));
+  LL_TRY(check_device(c));
+  LL_TRY(write_frames(c, layer, K_all, V_all, ll::recache_plan(f0, c->S, c->W), static_cast<hipStream_t>(stream),
+                      "recache launch"));
+  return ok();
+}
+
+ll_status ll_cache_recache_window(ll_cache* c, int layer, const void* K_win, const void* V_win, int n_frames,
+                                  void* stream) {
+  LL_TRY(check_layer(c, layer));
+  LL_TRY(check_tensor(K_win, "K_win"));
+  LL_TRY(check_tensor(V_win, "V_win"));
+  const int64_t f0 = c->f0[size_t(layer)];
+  const int64_t need = std::min<int64_t>(std::max<int64_t>(f0 - c->S, 0), c->W);
+  if (need == 0) return fail(LL_ERR_STATE, "recache_window: layer %d holds no window frames", layer);
+  if (n_frames != need)
+    return fail(LL_ERR_STATE, "recache_window: n_frames must equal min(max(f0-S,0), W) = %lld (got %d)",
+                (long long)need, n_frames);
+  LL_TRY(check_frames(c, n_frames));
+  LL_TRY(check_device(c));
+  LL_TRY(write_frames(c, layer, K_win, V_win, ll::recache_window_plan(f0, c->S, c->W),
+                      static_cast<hipStream_t>(stream), "recache_window launch"));
+  return ok();
+}
+
+ll_status ll_kv_project(const void* h, const void* W_K, const void* W_V, int n_tokens, int d_in, int d_out,
+                        void* K_all, void* V_all, void* stream) {
+  LL_TRY(check_tensor(h, "h"));
+  LL_TRY(check_tensor(W_K, "W_K"));
+  LL_TRY(check_tensor(W_V, "W_V"));
+  LL_TRY(check_tensor(K_all, "K_all"));
+  LL_TRY(check_tensor(V_all, "V_all"));
+  if (n_tokens < 1 || n_tokens > kMaxRows) return fail(LL_ERR_INVALID, "n_tokens out of range");
+  if (d_in < 64 || d_in % 64 != 0 || d_in > 65536) return fail(LL_ERR_INVALID, "d_in must be a multiple of 64");
+  if (d_out < 128 || d_out % 128 != 0 || d_out > 65536)
+    return fail(LL_ERR_INVALID, "d_out must be a multiple of 128");
+  ll::ProjParams p{};
+  p.h = static_cast<const uint16_t*>(h);
+  p.WK = static_cast<const uint16_t*>(W_K);
+  p.WV = static_cast<const uint16_t*>(W_V);
+  p.outK = static_cast<uint16_t*>(K_all);
+  p.outV = static_cast<uint16_t*>(V_all);
+  p.M = n_tokens;
+  p.K = d_in;
+  p.N = d_out;
+  hipError_t e = ll::launch_kv_project(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return ok();
+}
+
+ll_status ll_cache_frames_seen(const ll_cache* c, int layer, int64_t* f0) {
+  LL_TRY(check_layer(c, layer));
+  if (!f0) return fail(LL_ERR_INVALID, "f0 is NULL");
+  *f0 = c->f0[size_t(layer)];
+  return ok();
+}
+
+ll_status ll_cache_slot_frames(const ll_cache* c, int layer, int64_t* frame_of_slot) {
+  LL_TRY(check_layer(c, layer));
+  if (!frame_of_slot) return fail(LL_ERR_INVALID, "frame_of_slot is NULL");
+  const std::vector<int64_t>& sf = c->slot_frame[size_t(layer)];
+  std::memcpy(frame_of_slot, sf.data(), sf.size() * sizeof(int64_t));
+  return ok();
+}
+
+ll_status ll_cache_slot_view(const ll_cache* c, int layer, void** K, void** V, void** K_scale, void** V_scale) {
+  LL_TRY(check_layer(c, layer));
+  if (K) *K = c->k(layer);
+  if (V) *V = c->v(layer);
+  if (K_scale) *K_scale = c->ks(layer);
+  if (V_scale) *V_scale = c->vs(layer);
+  return ok();
+}
+
+}  // extern "C"

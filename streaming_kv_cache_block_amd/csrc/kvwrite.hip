@@ -1,0 +1,112 @@
+// kvwrite.hip -- write whole frames of K/V into cache slots (append/evict and recache).
+//
+// Append ("LongLive: Real-time Interactive Long Video Generation" explainer, dpshk.com,
+// §二: a finished chunk's K/V enter the cache; §五: frames older than the window are
+// evicted) and recache (§三 item 5: the recomputed cache replaces the old one) are the
+// same operation here: copy frame i of the caller's tensor into slot plan_slot[i].
+// Eviction is the overwrite of a ring slot; no memory is allocated or freed.
+//
+// bf16 caches: a frame is one contiguous run of T*H*D bf16 in both the source and the
+// slot, so this is a streaming 16-byte-vector copy (HBM bound).
+// int8 caches: each (token, head) row of D values is quantised on the fly
+//   a = max |x|, scale = a / 127, q = clamp(rint((x * 127) / a), -127, 127)
+// (every operation IEEE binary32, correctly rounded division, ties-to-even rounding;
+// x * 127 is exact for bf16 x).  LongLive-2.0 explainer, wmrh.cn, §15.2: the history
+// cache is stored in low precision to save memory and traffic.
+#include "device_common.h"
+#include "launch.h"
+
+namespace ll {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;   // 16-byte vectors in flight per thread
+
+// grid: x = block within the frame, y = plan entry, z = 0 (K) / 1 (V)
+__global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams p, int64_t vecs_per_frame) {
+  const int e = blockIdx.y;
+  const bool isv = blockIdx.z != 0;
+  const u32x4* src = reinterpret_cast<const u32x4*>(isv ? p.srcV : p.srcK) + int64_t(p.plan_src[e]) * vecs_per_frame;
+  u32x4* dst = reinterpret_cast<u32x4*>(isv ? p.dstV : p.dstK) + int64_t(p.plan_slot[e]) * vecs_per_frame;
+  const int64_t base = int64_t(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
+  u32x4 r[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + int64_t(u) * kThreads;
+    if (i < vecs_per_frame) r[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + int64_t(u) * kThreads;
+    if (i < vecs_per_frame) dst[i] = r[u];
+  }
+}
+
+// One (token, head) row of D values per LPR = D / 8 lanes; each lane owns 8 values.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int ROWS_PER_BLOCK = kThreads / LPR;
+  const int e = blockIdx.y;
+  const bool isv = blockIdx.z != 0;
+  const int64_t row_in_frame = int64_t(blockIdx.x) * ROWS_PER_BLOCK + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  const bool active = row_in_frame < p.rows_per_frame;
+  const int64_t src_row = int64_t(p.plan_src[e]) * p.rows_per_frame + row_in_frame;
+  const int64_t dst_row = int64_t(p.plan_slot[e]) * p.rows_per_frame + row_in_frame;
+
+  u32x4 w = {0, 0, 0, 0};
+  if (active) w = *reinterpret_cast<const u32x4*>((isv ? p.srcV : p.srcK) + src_row * D + 8 * sub);
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+    x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, LPR));
+
+  const float scale = a / 127.0f;
+  uint32_t packed[2] = {0u, 0u};
+  if (a > 0.0f) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float t = __builtin_rintf((x[k] * 127.0f) / a);
+      const int qi = int(fminf(fmaxf(t, -127.0f), 127.0f));
+      packed[k >> 2] |= (uint32_t(qi) & 0xffu) << (8 * (k & 3));
+    }
+  }
+  if (active) {
+    int8_t* dst = static_cast<int8_t*>(isv ? p.dstV : p.dstK);
+    *reinterpret_cast<u32x2*>(dst + dst_row * D + 8 * sub) = u32x2{packed[0], packed[1]};
+    if (sub == 0) (isv ? p.dstVs : p.dstKs)[dst_row] = scale;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const WriteParams& p, int D, bool kv_int8, hipStream_t s) {
+  if (p.n <= 0) return hipSuccess;
+  if (!kv_int8) {
+    const int64_t vecs = p.rows_per_frame * D * 2 / 16;
+    const int64_t per_block = int64_t(kThreads) * kUnroll;
+    dim3 grid(unsigned((vecs + per_block - 1) / per_block), unsigned(p.n), 2);
+    hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kThreads), 0, s, p, vecs);
+    return hipGetLastError();
+  }
+  const int rows_per_block = kThreads / (D / 8);
+  dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
+  if (D == 128) {
+    hipLaunchKernelGGL(quant_frames_kernel<128>, grid, dim3(kThreads), 0, s, p);
+  } else if (D == 64) {
+    hipLaunchKernelGGL(quant_frames_kernel<64>, grid, dim3(kThreads), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ll

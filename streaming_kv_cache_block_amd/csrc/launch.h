@@ -1,0 +1,61 @@
+// launch.h -- host-callable launchers of the device kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ll {
+
+constexpr int kMaxPlan = 128;  // = LL_MAX_SLOTS
+
+// One attention call: queries of one chunk against the cached slot prefix and the
+// chunk's own keys.  All token tensors are [tokens][H][D], row stride H*D elements.
+struct AttnParams {
+  const uint16_t* Q;
+  const uint16_t* Kc;   // own-chunk keys (bf16)
+  const uint16_t* Vc;   // own-chunk values (bf16)
+  uint16_t* out;
+  const void* cK;       // cached keys: bf16 or int8, slots [0, n_cache/T) contiguous
+  const void* cV;
+  const float* cKs;     // int8 only: per (token, head) scales
+  const float* cVs;
+  int nq;               // query rows = own-chunk key rows
+  int ncache;           // cached key rows
+  int H;
+  float c;              // log2(e) / sqrt(D)
+};
+
+hipError_t launch_attention(const AttnParams& p, int D, bool kv_int8, hipStream_t s);
+
+// Copy (bf16) or quantise (int8) whole frames of a [frames*T][H][D] bf16 tensor into
+// cache slots.  plan_src[i] is the frame index in the source tensor, plan_slot[i] the
+// destination slot, for i < n.
+struct WriteParams {
+  const uint16_t* srcK;
+  const uint16_t* srcV;
+  void* dstK;           // slot array of the layer: [S+W][T][H][D]
+  void* dstV;
+  float* dstKs;         // int8: [S+W][T][H]
+  float* dstVs;
+  int64_t rows_per_frame;  // T*H
+  int n;
+  int plan_src[kMaxPlan];
+  int plan_slot[kMaxPlan];
+};
+
+hipError_t launch_kv_write(const WriteParams& p, int D, bool kv_int8, hipStream_t s);
+
+// out[m][n] = sum_k h[m][k] * W[n][k] for W = W_K and W_V (bf16 in, fp32 sums,
+// bf16 out).  M rows, K = d_in (multiple of 64), N = d_out (multiple of 128).
+struct ProjParams {
+  const uint16_t* h;
+  const uint16_t* WK;
+  const uint16_t* WV;
+  uint16_t* outK;
+  uint16_t* outV;
+  int M, K, N;
+};
+
+hipError_t launch_kv_project(const ProjParams& p, hipStream_t s);
+
+}  // namespace ll

@@ -1,0 +1,143 @@
+"""GPU parity at the 1.3B-DiT shape: steady-state step, recache projection, int8 cache.
+
+Steady step: 12 heads, head_dim 128, 1560 tokens per frame, chunk 3, sink 3, window
+12, cache already full (10 seeded chunks appended, so the ring has wrapped), then 4
+denoise passes with fresh N(0, 0.5^2) bf16 inputs (seed 1) and one append.
+"""
+
+import time
+
+import numpy as np
+import pytest
+
+import streaming_kv_cache_block_amd as ll
+import synth
+from oracle import attention, bf16, gemm
+from synth import configs
+
+from helpers import History, check_slots, compare_attention, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ll.lib()
+    return torch
+
+
+def _log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def _prefill(cache, hist, cfg, layer, n_chunks, tag):
+    shape = (cfg.nq, cfg.heads, cfg.head_dim)
+    for k in range(n_chunks):
+        kb = synth.normal_bf16(shape, cfg.sigma, cfg.seed, tag, 1, layer, k)
+        vb = synth.normal_bf16(shape, cfg.sigma, cfg.seed, tag, 2, layer, k)
+        cache.append(layer, synth.to_device(kb), synth.to_device(vb))
+        hist.append(kb, vb)
+
+
+@pytest.mark.parametrize("kv_int8", [False, True])
+def test_steady_state_step(torch_gpu, kv_int8):
+    cfg = configs.STEADY
+    if kv_int8:   # the int8 workload's window
+        cfg = configs.Workload(**{**cfg.__dict__, "window": configs.LONG_INT8.window, "kv_int8": True,
+                                  "prefill_chunks": 9, "seed": configs.LONG_INT8.seed})
+    C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8" if kv_int8 else "bf16")
+    hist = History(S, W, T)
+    _prefill(cache, hist, cfg, 0, cfg.prefill_chunks, 100)
+    check_slots(cache, 0, hist, kv_int8=kv_int8)
+    f0 = hist.f0
+    shape = (cfg.nq, H, D)
+    rows = sample_rows(cfg.nq, T, seed=cfg.seed)
+    for p in range(cfg.passes):
+        q, kc, vc = (synth.normal_bf16(shape, cfg.sigma, cfg.seed, t, 0, 0, p) for t in range(3))
+        out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+        t0 = time.time()
+        if p == 0:
+            ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv_int8=kv_int8)
+            mx, mn = compare_attention(out, ref, f"pass {p} (all rows)")
+        else:
+            ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv_int8=kv_int8, rows=rows)
+            mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"pass {p} (sampled rows)")
+        _log(f"steady int8={kv_int8} pass {p}: max-abs {mx:.2e} mean-abs {mn:.2e} oracle {time.time() - t0:.1f}s")
+    cache.append(0, synth.to_device(kc), synth.to_device(vc))
+    hist.append(kc, vc)
+    check_slots(cache, 0, hist, kv_int8=kv_int8)
+
+
+def test_projection_identity_and_small_integers_bit_exact(torch_gpu):
+    torch = torch_gpu
+    n, d = 777, 256
+    h = synth.normal_bf16((n, d), 1.0, 3, 500)
+    eye = bf16.round_f32(np.eye(d, dtype=np.float32))
+    K, V = ll.kv_project(synth.to_device(h), synth.to_device(eye), synth.to_device(eye))
+    assert np.array_equal(synth.to_bits(K), h) and np.array_equal(synth.to_bits(V), h)
+    rng = np.random.default_rng(4)
+    hi = bf16.round_f32(rng.integers(-8, 9, size=(n, 192)).astype(np.float32))
+    wi = bf16.round_f32(rng.integers(-8, 9, size=(128, 192)).astype(np.float32))
+    K, _ = ll.kv_project(synth.to_device(hi), synth.to_device(wi), synth.to_device(wi))
+    assert np.array_equal(synth.to_bits(K), gemm.project_bf16(hi, wi))
+
+
+def _projection_bound_violations(got_bits, h_bits, w_bits):
+    """Count outputs outside the error bound of fp32 accumulation + one bf16 rounding.
+
+    Any order of n fp32 additions of exact bf16 x bf16 products satisfies
+    |s - exact| <= gamma_n * sum |h_k w_k|, gamma_n = n u / (1 - n u), u = 2^-24;
+    rounding s to bf16 adds at most half an ulp of the result.  The oracle's own
+    fp32 result obeys the same bound, so it is checked the same way.
+    """
+    h = bf16.to_f64(h_bits)
+    w = bf16.to_f64(w_bits)
+    exact = h @ w.T
+    absum = np.abs(h) @ np.abs(w).T
+    n = h.shape[1]
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    got = bf16.to_f64(got_bits)
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126))) - 8)
+    bound = half_ulp + gamma * absum
+    bad = np.abs(got - exact) > bound
+    return int(bad.sum()), float(np.abs(got - exact).max())
+
+
+def test_recache_projection_then_rewrite_then_attention(torch_gpu):
+    """Recache at a prompt switch at full size (one layer): K = h W_K^T, V = h W_V^T for
+    the 15 retained frames, rewrite of every slot, then the next chunk's attention."""
+    cfg = configs.RECACHE
+    C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
+    hid = cfg.hidden
+    cache = ll.Cache(1, H, D, T, S, W)
+    hist = History(S, W, T)
+    _prefill(cache, hist, cfg, 0, cfg.prefill_chunks, 200)
+    n = min(hist.f0, S + W)
+    h = synth.normal_bf16((n * T, hid), 1.0, cfg.seed, 10, 0)
+    wk = synth.normal_bf16((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 11, 0)
+    wv = synth.normal_bf16((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 12, 0)
+    K, V = ll.kv_project(synth.to_device(h), synth.to_device(wk), synth.to_device(wv))
+    kb, vb = synth.to_bits(K), synth.to_bits(V)
+    t0 = time.time()
+    for got, w in ((kb, wk), (vb, wv)):
+        ref = gemm.project_bf16(h, w)
+        nbad, mx = _projection_bound_violations(got, h, w)
+        assert nbad == 0, f"{nbad} GPU outputs outside the accumulation bound (max diff {mx})"
+        nbad, mx = _projection_bound_violations(ref, h, w)
+        assert nbad == 0, f"{nbad} oracle outputs outside the accumulation bound (max diff {mx})"
+        assert np.mean(got != ref) < 0.01    # differences are rare rounding flips
+    _log(f"projection checked in {time.time() - t0:.1f}s")
+    cache.recache(0, K.view(n * T, H, D), V.view(n * T, H, D))
+    hist.recache(kb.reshape(n * T, H, D), vb.reshape(n * T, H, D))
+    check_slots(cache, 0, hist)
+    shape = (cfg.nq, H, D)
+    q, kc, vc = (synth.normal_bf16(shape, 0.5, cfg.seed, t, 20, 0) for t in range(3))
+    out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+    rows = sample_rows(cfg.nq, T, seed=3)
+    ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, rows=rows)
+    compare_attention(synth.to_bits(out)[rows], ref, "attention after recache")
