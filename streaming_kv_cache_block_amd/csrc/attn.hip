@@ -3,52 +3,68 @@
 // Computes, per head, softmax((Q K^T) / sqrt(D)) V of one chunk's queries over
 //   segment 1: the cached slots [0, n_vis) (sink frames, then the window ring in
 //              physical order -- "LongLive: Real-time Interactive Long Video
-//              Generation" explainer, dpshk.com, §五 and §六: context = sink frames
-//              plus the recent window);
+//              Generation" explainer, dpshk.com, §五 and §六: the context is the
+//              sink frames plus the recent window);
 //   segment 2: the chunk's own keys, all visible (block-causal mask, LongLive-2.0
 //              explainer, wmrh.cn, §6: a chunk sees earlier chunks and itself).
-// Nothing else is touched: evicted history is not in memory at all, and no mask is
-// materialised -- the two segments ARE the visible set.
+// Evicted history is not in memory and no mask is materialised: the two segments
+// are the visible set, walked in tiles of 64 keys; only a segment's last tile is
+// partial.
 //
-// Kernel structure (one workgroup = 4 waves, one head, 32*NQB query rows per wave):
+// Workgroup = 4 waves, one head, 32*NQB query rows per wave (NQB 32-row blocks).
 //   * Q fragments stay in registers for the whole key walk.
-//   * Keys are walked in tiles of 64 rows; each tile of K and V goes global ->
-//     registers -> LDS (double-buffered, one barrier per tile) and is shared by
-//     the 4 waves.  V is written to LDS transposed (V^T[d][key]) because the P*V
-//     product contracts over keys; an XOR swizzle of 4-key quads keeps both the
-//     transposed writes and the MFMA operand reads free of bank conflicts.
-//   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
-//     each lane then holds one query's scores for 16 keys, so the running row max
-//     needs one exchange with lane ^ 32 and the row sum is kept per lane (the two
-//     halves are added once at the end).  The probabilities of the lane ARE the
-//     MFMA B operand of O^T = V^T P^T: the keys of the lane's 8 B-slots are
-//     matched by reading V^T at the same keys, so no register shuffle is needed.
-//   * Online softmax in base 2 with log2(e)/sqrt(D) folded into one FMA.
-//   * int8 caches: codes are widened to bf16 while staged into LDS (exact), the
-//     per-key K scale multiplies the score column and the per-key V scale
-//     multiplies the probability column before it is rounded to bf16
-//     (LongLive-2.0 explainer, wmrh.cn, §15.3: dequantisation must not become a
-//     separate slow pass).
+//   * K and V tiles live in LDS in their natural [key][d] layout, double-buffered,
+//     one barrier per tile.  16-byte chunks are XOR-swizzled per row so that the
+//     MFMA operand reads below are free of bank conflicts.  bf16 tiles are copied
+//     global -> LDS by the load-to-LDS path (no registers); int8 cache tiles are
+//     widened to bf16 in registers on the way (exact for |q| <= 127).
+//   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA: a
+//     lane then holds one query's scores for 16 keys of each 32-key block, so the
+//     running row max needs one exchange with lane ^ 32 and the row sum stays per
+//     lane until the end.  Each K fragment read from LDS feeds NQB MFMAs.
+//   * The lane's probabilities are the B operand of O^T = V^T P^T as they are; the
+//     A operand V^T (8 keys of one d per lane, keys matched to the lane's B slots)
+//     comes from two transpose reads (ds_read_b64_tr_b16) of the natural V tile.
+//   * Online softmax in base 2, log2(e)/sqrt(D) folded into one FMA; the running
+//     max is only raised (and O, l rescaled) when a score exceeds it by more than
+//     2^8, which keeps every probability <= 256 and skips almost all rescales.
+//   * int8 caches: the per-key K scale multiplies the score column and the V scale
+//     the probability column before rounding to bf16 (LongLive-2.0 explainer,
+//     wmrh.cn, §15.3: dequantisation fused into the consumer, not a separate pass).
+//   * Workgroups are numbered so that the query tiles of one head run on the same
+//     XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs) and share
+//     its L2 while they stream the same keys.
 #include "device_common.h"
 #include "launch.h"
 
 namespace ll {
 namespace {
 
-constexpr int BN = 64;        // keys per tile
-constexpr int NTHREADS = 256; // 4 waves
+constexpr int BN = 64;         // keys per tile
+constexpr int NTHREADS = 256;  // 4 waves
+constexpr int NXCD = 8;
+constexpr float kLazyThreshold = 8.0f;   // log2 units
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
 template <int D>
 struct Geo {
-  static constexpr int KP = D + 8;          // K row pitch in LDS (elements): 16 B pad
-  static constexpr int CH = D / 8;          // 8-element chunks per row
-  static constexpr int KPASS = BN * CH / NTHREADS;  // 16-B K chunks per thread per tile
-  static constexpr int K_ELEMS = BN * KP;
-  static constexpr int V_ELEMS = D * BN;    // V^T[d][key], 128 B rows, swizzled quads
+  static constexpr int CH = D / 8;                     // 16-byte chunks per row
+  static constexpr int ROWS_PER_DMA = 64 / CH;         // rows one wave-wide 1 KB copy covers
+  static constexpr int DMA_PER_WAVE = BN / ROWS_PER_DMA / 4;
+  static constexpr int REG_PASS = BN * CH / NTHREADS;  // int8 staging: chunks per thread
+  static constexpr int TILE = BN * D;                  // elements per K (or V) tile
 };
 
-// quad (4 keys = 8 bytes) position of key quad `q` in V^T row `d`
-__device__ __forceinline__ int vt_quad(int d, int q) { return q ^ ((d ^ (d >> 3)) & 15); }
+// Swizzled chunk position of chunk c in row r.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  else return c ^ (((r & 1) << 2) | ((r >> 1) & 3));
+}
 
 struct TileInfo {
   int seg;    // 0 = cache, 1 = own chunk
@@ -70,129 +86,94 @@ __device__ __forceinline__ TileInfo tile_info(int j, int n1, int ncache, int nq)
   return t;
 }
 
-template <int D, bool KV8>
-struct Stage {
+// bf16 tile: every wave copies its share of rows straight into LDS.  Rows past the
+// segment end re-read the last valid row (its scores are masked to -inf and its
+// values then get probability 0, so the data only has to be finite).
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint16_t* gk, const uint16_t* gv, int64_t rs, const TileInfo& ti,
+                                         uint16_t* lk, uint16_t* lv, int wave, int lane) {
   using G = Geo<D>;
-  u32x4 k[G::KPASS];     // bf16 K chunks
-  u32x4 v[4];            // bf16 V chunks: 4 keys x 8 d
-  u32x2 k8[G::KPASS];    // int8 K chunks (cache tiles of int8 caches)
-  u32x2 v8[4];
-  float sc;              // K scale (threads 0..63) or V scale (64..127)
-};
-
-template <int D, bool KV8>
-__device__ __forceinline__ void load_tile(Stage<D, KV8>& st, const AttnParams& p, const TileInfo& ti,
-                                          int h, int tid) {
-  using G = Geo<D>;
-  const int64_t rs = int64_t(p.H) * D;   // row stride (elements)
-  const int c = tid % G::CH;
-  const bool int8_tile = KV8 && ti.seg == 0;
-  // K: rows tid / CH + (NTHREADS / CH) * i
 #pragma unroll
-  for (int i = 0; i < G::KPASS; ++i) {
-    const int r = tid / G::CH + (NTHREADS / G::CH) * i;
-    const bool ok = r < ti.cnt;
-    const int64_t off = int64_t(ti.start + r) * rs + int64_t(h) * D + 8 * c;
-    if (int8_tile) {
-      st.k8[i] = ok ? *reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(p.cK) + off) : u32x2{0, 0};
-    } else {
-      const uint16_t* base = ti.seg == 0 ? static_cast<const uint16_t*>(p.cK) : p.Kc;
-      st.k[i] = ok ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
-    }
-  }
-  // V: 4 consecutive keys 4*kq .. 4*kq+3, chunk c
-  const int kq = tid / G::CH;
-  if (kq < BN / 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * kq + i;
-      const bool ok = r < ti.cnt;
-      const int64_t off = int64_t(ti.start + r) * rs + int64_t(h) * D + 8 * c;
-      if (int8_tile) {
-        st.v8[i] = ok ? *reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(p.cV) + off) : u32x2{0, 0};
-      } else {
-        const uint16_t* base = ti.seg == 0 ? static_cast<const uint16_t*>(p.cV) : p.Vc;
-        st.v[i] = ok ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-  if (KV8) {
-    st.sc = 1.0f;
-    if (int8_tile && tid < 2 * BN) {
-      const int r = tid % BN;
-      const float* sp = tid < BN ? p.cKs : p.cVs;
-      st.sc = r < ti.cnt ? sp[int64_t(ti.start + r) * p.H + h] : 0.0f;
-    }
+  for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
+    const int r0 = (wave * G::DMA_PER_WAVE + i) * G::ROWS_PER_DMA;
+    const int r = r0 + lane / G::CH;
+    const int c = swz<D>(r, lane % G::CH);
+    const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 8 * c;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(gk + off), (lds_void*)(lk + r0 * D), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void*)(gv + off), (lds_void*)(lv + r0 * D), 16, 0, 0);
   }
 }
 
-template <int D, bool KV8>
-__device__ __forceinline__ void store_tile(const Stage<D, KV8>& st, uint16_t* ks, uint16_t* vt, float* kscl,
-                                           float* vscl, const TileInfo& ti, int tid) {
+template <int D>
+struct Stage8 {
+  u32x2 k[Geo<D>::REG_PASS];
+  u32x2 v[Geo<D>::REG_PASS];
+  float sc;
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile8(Stage8<D>& st, const AttnParams& p, int h, const TileInfo& ti, int tid) {
   using G = Geo<D>;
-  const int c = tid % G::CH;
-  const bool int8_tile = KV8 && ti.seg == 0;
+  const int64_t rs = int64_t(p.H) * D;
+  const int8_t* gk = static_cast<const int8_t*>(p.cK) + int64_t(h) * D;
+  const int8_t* gv = static_cast<const int8_t*>(p.cV) + int64_t(h) * D;
 #pragma unroll
-  for (int i = 0; i < G::KPASS; ++i) {
+  for (int i = 0; i < G::REG_PASS; ++i) {
     const int r = tid / G::CH + (NTHREADS / G::CH) * i;
-    u32x4 w;
-    if (int8_tile) {
-      w = u32x4{i8x2_to_bf16x2(st.k8[i].x, 0), i8x2_to_bf16x2(st.k8[i].x, 2),
-                i8x2_to_bf16x2(st.k8[i].y, 0), i8x2_to_bf16x2(st.k8[i].y, 2)};
-    } else {
-      w = st.k[i];
-    }
-    *reinterpret_cast<u32x4*>(ks + r * G::KP + 8 * c) = w;
+    const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 8 * (tid % G::CH);
+    st.k[i] = *reinterpret_cast<const u32x2*>(gk + off);
+    st.v[i] = *reinterpret_cast<const u32x2*>(gv + off);
   }
-  const int kq = tid / G::CH;
-  if (kq < BN / 4) {
-    u32x4 rv[4];
+  st.sc = 0.0f;
+  if (tid < 2 * BN) {
+    const int r = tid % BN;
+    const float* sp = tid < BN ? p.cKs : p.cVs;
+    st.sc = r < ti.cnt ? sp[int64_t(ti.start + r) * p.H + h] : 0.0f;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile8(const Stage8<D>& st, uint16_t* lk, uint16_t* lv, float* lks, float* lvs,
+                                            int tid) {
+  using G = Geo<D>;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (int8_tile) {
-        rv[i] = u32x4{i8x2_to_bf16x2(st.v8[i].x, 0), i8x2_to_bf16x2(st.v8[i].x, 2),
-                      i8x2_to_bf16x2(st.v8[i].y, 0), i8x2_to_bf16x2(st.v8[i].y, 2)};
-      } else {
-        rv[i] = st.v[i];
-      }
-    }
-    // rv[i] holds V[4kq+i][8c .. 8c+7]; write V^T[8c+j][4kq .. 4kq+3] for j < 8
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = 8 * c + j;
-      const int w = j >> 1;
-      u32x2 q;
-      if (j & 1) {
-        q.x = pick_hi_hi(rv[0][w], rv[1][w]);
-        q.y = pick_hi_hi(rv[2][w], rv[3][w]);
-      } else {
-        q.x = pick_lo_lo(rv[0][w], rv[1][w]);
-        q.y = pick_lo_lo(rv[2][w], rv[3][w]);
-      }
-      *reinterpret_cast<u32x2*>(vt + d * BN + 4 * vt_quad(d, kq)) = q;
-    }
+  for (int i = 0; i < G::REG_PASS; ++i) {
+    const int r = tid / G::CH + (NTHREADS / G::CH) * i;
+    const int pos = r * D + 8 * swz<D>(r, tid % G::CH);
+    *reinterpret_cast<u32x4*>(lk + pos) = u32x4{i8x2_to_bf16x2(st.k[i].x, 0), i8x2_to_bf16x2(st.k[i].x, 2),
+                                                i8x2_to_bf16x2(st.k[i].y, 0), i8x2_to_bf16x2(st.k[i].y, 2)};
+    *reinterpret_cast<u32x4*>(lv + pos) = u32x4{i8x2_to_bf16x2(st.v[i].x, 0), i8x2_to_bf16x2(st.v[i].x, 2),
+                                                i8x2_to_bf16x2(st.v[i].y, 0), i8x2_to_bf16x2(st.v[i].y, 2)};
   }
-  if (KV8 && tid < 2 * BN) {
-    (tid < BN ? kscl : vscl)[tid % BN] = st.sc;
-  }
+  if (tid < 2 * BN) (tid < BN ? lks : lvs)[tid % BN] = st.sc;
 }
 
 template <int D, int NQB, bool KV8>
-__global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
+__global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p, int n_qtiles, int n_blocks) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sm_k[2][G::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_v[2][G::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_k[2][G::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_v[2][G::TILE];
   __shared__ __attribute__((aligned(16))) float sm_ks[KV8 ? 2 : 1][BN];
   __shared__ __attribute__((aligned(16))) float sm_vs[KV8 ? 2 : 1][BN];
+
+  // XCD-aware numbering: hardware deals block ids round-robin over the XCDs; give
+  // each XCD a contiguous range of logical blocks (query tiles of the same head).
+  const int per_xcd = (n_blocks + NXCD - 1) / NXCD;
+  const int bid = blockIdx.x;
+  const int logical = (bid % NXCD) * per_xcd + bid / NXCD;
+  if (logical >= n_blocks) return;
+  const int h = logical / n_qtiles;
+  const int qtile = logical % n_qtiles;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = lane >> 5;     // lane half
+  const int g = lane >> 5;           // lane half
   const int r32 = lane & 31;
-  const int h = blockIdx.y;
+  const int s16 = lane & 15;         // lane within its 16-lane group
+  const int h16 = (lane >> 4) & 1;   // 16-lane group within the half
   const int64_t rs = int64_t(p.H) * D;
-  const int q0 = blockIdx.x * (4 * 32 * NQB) + wave * (32 * NQB);
+  const int q0 = qtile * (4 * 32 * NQB) + wave * (32 * NQB);
 
   // Q^T fragments (MFMA B operand): lane holds query r32, d = 16 s + 8 g + [0, 8)
   bf16x8 qf[NQB][D / 16];
@@ -220,23 +201,35 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
   const int n1 = (p.ncache + BN - 1) / BN;
   const int ntiles = n1 + (p.nq + BN - 1) / BN;
   const float c = p.c;
+  const uint16_t* ck = KV8 ? nullptr : static_cast<const uint16_t*>(p.cK) + int64_t(h) * D;
+  const uint16_t* cv = KV8 ? nullptr : static_cast<const uint16_t*>(p.cV) + int64_t(h) * D;
+  const uint16_t* kc = p.Kc + int64_t(h) * D;
+  const uint16_t* vc = p.Vc + int64_t(h) * D;
 
-  Stage<D, KV8> st;
+  Stage8<D> st8;
   TileInfo ti = tile_info(0, n1, p.ncache, p.nq);
-  load_tile<D, KV8>(st, p, ti, h, tid);
-  store_tile<D, KV8>(st, sm_k[0], sm_v[0], sm_ks[0], sm_vs[0], ti, tid);
+  if (KV8 && ti.seg == 0) {
+    load_tile8<D>(st8, p, h, ti, tid);
+    store_tile8<D>(st8, sm_k[0], sm_v[0], sm_ks[0], sm_vs[0], tid);
+  } else {
+    dma_tile<D>(ti.seg == 0 ? ck : kc, ti.seg == 0 ? cv : vc, rs, ti, sm_k[0], sm_v[0], wave, lane);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
     const TileInfo cur = ti;
     const bool more = j + 1 < ntiles;
+    bool next8 = false;
     if (more) {
       ti = tile_info(j + 1, n1, p.ncache, p.nq);
-      load_tile<D, KV8>(st, p, ti, h, tid);
+      next8 = KV8 && ti.seg == 0;
+      if (next8) load_tile8<D>(st8, p, h, ti, tid);
+      else dma_tile<D>(ti.seg == 0 ? ck : kc, ti.seg == 0 ? cv : vc, rs, ti, sm_k[buf ^ 1], sm_v[buf ^ 1], wave, lane);
     }
-    const uint16_t* ks = sm_k[buf];
-    const uint16_t* vt = sm_v[buf];
+    const uint16_t* lk = sm_k[buf];
+    const uint16_t* lv = sm_v[buf];
 
     // ---- S^T = K Q^T for 64 keys (two 32-key blocks) ----
     f32x16 S[NQB][2];
@@ -244,8 +237,9 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
     for (int qb = 0; qb < NQB; ++qb) S[qb][0] = S[qb][1] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + r32 * G::KP + 16 * s + 8 * g));
-      const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 + r32) * G::KP + 16 * s + 8 * g));
+      const int ch = 2 * s + g;
+      const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + r32 * D + 8 * swz<D>(r32, ch)));
+      const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + (32 + r32) * D + 8 * swz<D>(32 + r32, ch)));
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         S[qb][0] = mfma32(k0, qf[qb][s], S[qb][0]);
@@ -273,15 +267,14 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int key = 32 * b + 8 * i + 4 * g + jj;
-            if (key >= cur.cnt) {
+            if (32 * b + 8 * i + 4 * g + jj >= cur.cnt) {
 #pragma unroll
               for (int qb = 0; qb < NQB; ++qb) S[qb][b][4 * i + jj] = -__builtin_inff();
             }
           }
     }
 
-    // ---- online softmax (base 2) ----
+    // ---- online softmax (base 2, lazy rescale) ----
     bf16x8 P[NQB][4];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -290,22 +283,26 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[qb][b][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx * c);
-      const float alpha = fast_exp2(m[qb] - mnew);
-      m[qb] = mnew;
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kLazyThreshold)) {
+        const float mnew = fmaxf(m[qb], mx);
+        const float alpha = fast_exp2(m[qb] - mnew);
+        m[qb] = mnew;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) O[qb][e] *= alpha;
+      }
+      const float mq = m[qb];
       float rsum = 0.0f;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float e = fast_exp2(__builtin_fmaf(S[qb][b][v], c, -mnew));
+          const float e = fast_exp2(__builtin_fmaf(S[qb][b][v], c, -mq));
           rsum += e;
           S[qb][b][v] = e;
         }
-      l[qb] = l[qb] * alpha + rsum;
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) O[qb][e] *= alpha;
+      l[qb] += rsum;
       if (scaled) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -329,24 +326,32 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
     }
 
     // ---- O^T += V^T P^T ----
+    // B slot t of step u holds key 32 (u>>1) + 16 (u&1) + 8 (t>>2) + 4 g + (t&3).  The
+    // transpose read gives lane s16 of a 16-lane group element (s16 & 3) of the rows
+    // addressed by lanes (s16 >> 2) + 4 k, k = 0..3: lane s16 therefore addresses key
+    // row kA + (s16 >> 2), columns d0 + 4 (s16 & 3) .. + 3.
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) {
-      const int d = 32 * e + r32;
+      const int dcol = 32 * e + 16 * h16 + 4 * (s16 & 3);
+      const int dch = dcol >> 3, dhalf = dcol & 7;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int qd1 = 8 * (u >> 1) + 4 * (u & 1) + g;   // quad of keys 32b + 16(u&1) + 4g
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + d * BN + 4 * vt_quad(d, qd1));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + d * BN + 4 * vt_quad(d, qd1 + 2));
-        const bf16x8 vf = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+        const int kA = 32 * (u >> 1) + 16 * (u & 1) + 4 * g + (s16 >> 2);
+        const int kB = kA + 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(lv + kA * D + 8 * swz<D>(kA, dch) + dhalf));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(lv + kB * D + 8 * swz<D>(kB, dch) + dhalf));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) O[qb][e] = mfma32(vf, P[qb][u], O[qb][e]);
       }
     }
 
-    if (more) {
-      const int nb = buf ^ 1;
-      store_tile<D, KV8>(st, sm_k[nb], sm_v[nb], sm_ks[KV8 ? nb : 0], sm_vs[KV8 ? nb : 0], ti, tid);
+    if (next8) {
+      store_tile8<D>(st8, sm_k[buf ^ 1], sm_v[buf ^ 1], sm_ks[KV8 ? buf ^ 1 : 0], sm_vs[KV8 ? buf ^ 1 : 0], tid);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -374,8 +379,10 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p) {
 template <int D, int NQB, bool KV8>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const int rows = 4 * 32 * NQB;
-  dim3 grid((p.nq + rows - 1) / rows, p.H);
-  hipLaunchKernelGGL((attn_kernel<D, NQB, KV8>), grid, dim3(NTHREADS), 0, s, p);
+  const int n_qtiles = (p.nq + rows - 1) / rows;
+  const int n_blocks = n_qtiles * p.H;
+  const int grid = (n_blocks + NXCD - 1) / NXCD * NXCD;
+  hipLaunchKernelGGL((attn_kernel<D, NQB, KV8>), dim3(grid), dim3(NTHREADS), 0, s, p, n_qtiles, n_blocks);
   return hipGetLastError();
 }
 
@@ -384,9 +391,8 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
 hipError_t launch_attention(const AttnParams& p, int D, bool kv_int8, hipStream_t s) {
   const bool big = p.nq > 4 * 32;
   if (D == 128) {
-    // one 32-row block per wave: two blocks per wave exceed the register file
-    if (kv_int8) return launch_t<128, 1, true>(p, s);
-    return launch_t<128, 1, false>(p, s);
+    if (kv_int8) return big ? launch_t<128, 2, true>(p, s) : launch_t<128, 1, true>(p, s);
+    return big ? launch_t<128, 2, false>(p, s) : launch_t<128, 1, false>(p, s);
   }
   if (D == 64) {
     if (kv_int8) return big ? launch_t<64, 2, true>(p, s) : launch_t<64, 1, true>(p, s);
