@@ -11,7 +11,7 @@
 // are the visible set, walked in tiles of 64 keys; only a segment's last tile is
 // partial.
 //
-// Workgroup = 4 waves, one head, 32*NQB query rows per wave (NQB 32-row blocks).
+// Workgroup = NW waves, one head, 32*NQB query rows per wave (NQB 32-row blocks).
 //   * Q fragments stay in registers for the whole key walk.
 //   * K and V tiles live in LDS in their natural [key][d] layout, double-buffered,
 //     one barrier per tile.  16-byte chunks are XOR-swizzled per row so that the
@@ -34,6 +34,8 @@
 //   * Workgroups are numbered so that the query tiles of one head run on the same
 //     XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs) and share
 //     its L2 while they stream the same keys.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -41,7 +43,6 @@ namespace ll {
 namespace {
 
 constexpr int BN = 64;         // keys per tile
-constexpr int NTHREADS = 256;  // 4 waves
 constexpr int NXCD = 8;
 constexpr float kLazyThreshold = 8.0f;   // log2 units
 
@@ -50,13 +51,15 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-template <int D>
+template <int D, int NW>
 struct Geo {
+  static constexpr int NT = 64 * NW;                   // threads per workgroup
   static constexpr int CH = D / 8;                     // 16-byte chunks per row
   static constexpr int ROWS_PER_DMA = 64 / CH;         // rows one wave-wide 1 KB copy covers
-  static constexpr int DMA_PER_WAVE = BN / ROWS_PER_DMA / 4;
-  static constexpr int REG_PASS = BN * CH / NTHREADS;  // int8 staging: chunks per thread
+  static constexpr int DMA_PER_WAVE = BN / ROWS_PER_DMA / NW;
+  static constexpr int REG_PASS = BN * CH / NT;        // int8 staging: chunks per thread
   static constexpr int TILE = BN * D;                  // elements per K (or V) tile
+  static_assert(DMA_PER_WAVE >= 1 && REG_PASS >= 1 && NT >= 2 * BN, "tile split");
 };
 
 // Swizzled chunk position of chunk c in row r.
@@ -64,6 +67,12 @@ template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
   else return c ^ (((r & 1) << 2) | ((r >> 1) & 3));
+}
+
+// Element offset of chunk c of row r in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz_row_base(int r, int c) {
+  return r * D + 8 * swz<D>(r, c);
 }
 
 struct TileInfo {
@@ -89,10 +98,10 @@ __device__ __forceinline__ TileInfo tile_info(int j, int n1, int ncache, int nq)
 // bf16 tile: every wave copies its share of rows straight into LDS.  Rows past the
 // segment end re-read the last valid row (its scores are masked to -inf and its
 // values then get probability 0, so the data only has to be finite).
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void dma_tile(const uint16_t* gk, const uint16_t* gv, int64_t rs, const TileInfo& ti,
                                          uint16_t* lk, uint16_t* lv, int wave, int lane) {
-  using G = Geo<D>;
+  using G = Geo<D, NW>;
 #pragma unroll
   for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
     const int r0 = (wave * G::DMA_PER_WAVE + i) * G::ROWS_PER_DMA;
@@ -104,22 +113,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* gk, const uint16_t* gv,
   }
 }
 
-template <int D>
+template <int D, int NW>
 struct Stage8 {
-  u32x2 k[Geo<D>::REG_PASS];
-  u32x2 v[Geo<D>::REG_PASS];
+  u32x2 k[Geo<D, NW>::REG_PASS];
+  u32x2 v[Geo<D, NW>::REG_PASS];
   float sc;
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile8(Stage8<D>& st, const AttnParams& p, int h, const TileInfo& ti, int tid) {
-  using G = Geo<D>;
+template <int D, int NW>
+__device__ __forceinline__ void load_tile8(Stage8<D, NW>& st, const AttnParams& p, int h, const TileInfo& ti,
+                                           int tid) {
+  using G = Geo<D, NW>;
   const int64_t rs = int64_t(p.H) * D;
   const int8_t* gk = static_cast<const int8_t*>(p.cK) + int64_t(h) * D;
   const int8_t* gv = static_cast<const int8_t*>(p.cV) + int64_t(h) * D;
 #pragma unroll
   for (int i = 0; i < G::REG_PASS; ++i) {
-    const int r = tid / G::CH + (NTHREADS / G::CH) * i;
+    const int r = tid / G::CH + (G::NT / G::CH) * i;
     const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 8 * (tid % G::CH);
     st.k[i] = *reinterpret_cast<const u32x2*>(gk + off);
     st.v[i] = *reinterpret_cast<const u32x2*>(gv + off);
@@ -132,13 +142,13 @@ __device__ __forceinline__ void load_tile8(Stage8<D>& st, const AttnParams& p, i
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile8(const Stage8<D>& st, uint16_t* lk, uint16_t* lv, float* lks, float* lvs,
-                                            int tid) {
-  using G = Geo<D>;
+template <int D, int NW>
+__device__ __forceinline__ void store_tile8(const Stage8<D, NW>& st, uint16_t* lk, uint16_t* lv, float* lks,
+                                            float* lvs, int tid) {
+  using G = Geo<D, NW>;
 #pragma unroll
   for (int i = 0; i < G::REG_PASS; ++i) {
-    const int r = tid / G::CH + (NTHREADS / G::CH) * i;
+    const int r = tid / G::CH + (G::NT / G::CH) * i;
     const int pos = r * D + 8 * swz<D>(r, tid % G::CH);
     *reinterpret_cast<u32x4*>(lk + pos) = u32x4{i8x2_to_bf16x2(st.k[i].x, 0), i8x2_to_bf16x2(st.k[i].x, 2),
                                                 i8x2_to_bf16x2(st.k[i].y, 0), i8x2_to_bf16x2(st.k[i].y, 2)};
@@ -148,133 +158,116 @@ __device__ __forceinline__ void store_tile8(const Stage8<D>& st, uint16_t* lk, u
   if (tid < 2 * BN) (tid < BN ? lks : lvs)[tid % BN] = st.sc;
 }
 
-template <int D, int NQB, bool KV8>
-__global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p, int n_qtiles, int n_blocks) {
-  using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sm_k[2][G::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_v[2][G::TILE];
-  __shared__ __attribute__((aligned(16))) float sm_ks[KV8 ? 2 : 1][BN];
-  __shared__ __attribute__((aligned(16))) float sm_vs[KV8 ? 2 : 1][BN];
-
-  // XCD-aware numbering: hardware deals block ids round-robin over the XCDs; give
-  // each XCD a contiguous range of logical blocks (query tiles of the same head).
-  const int per_xcd = (n_blocks + NXCD - 1) / NXCD;
-  const int bid = blockIdx.x;
-  const int logical = (bid % NXCD) * per_xcd + bid / NXCD;
-  if (logical >= n_blocks) return;
-  const int h = logical / n_qtiles;
-  const int qtile = logical % n_qtiles;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 5;           // lane half
-  const int r32 = lane & 31;
-  const int s16 = lane & 15;         // lane within its 16-lane group
-  const int h16 = (lane >> 4) & 1;   // 16-lane group within the half
-  const int64_t rs = int64_t(p.H) * D;
-  const int q0 = qtile * (4 * 32 * NQB) + wave * (32 * NQB);
-
-  // Q^T fragments (MFMA B operand): lane holds query r32, d = 16 s + 8 g + [0, 8)
-  bf16x8 qf[NQB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = q0 + 32 * qb + r32;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 w = {0, 0, 0, 0};
-      if (row < p.nq) w = *reinterpret_cast<const u32x4*>(p.Q + int64_t(row) * rs + int64_t(h) * D + 16 * s + 8 * g);
-      qf[qb][s] = as_bf16x8(w);
-    }
+// Order of the key tiles: the (at most two) partial tiles -- the last tile of each
+// segment -- come first, so that the long run of full tiles after them carries no
+// masking code.  Softmax attention does not depend on the order of its keys.
+struct TileOrder {
+  int n1, n2, np1, np2, ncache, nq;
+  __device__ TileOrder(int ncache_, int nq_) : ncache(ncache_), nq(nq_) {
+    n1 = (ncache + BN - 1) / BN;
+    n2 = (nq + BN - 1) / BN;
+    np1 = (ncache % BN) != 0;
+    np2 = (nq % BN) != 0;
   }
+  __device__ int npart() const { return np1 + np2; }
+  __device__ int full1_end() const { return np1 + np2 + n1 - np1; }   // end of full cache tiles
+  __device__ int total() const { return n1 + n2; }
+  __device__ TileInfo at(int j) const {
+    TileInfo t;
+    if (j < np1 + np2) {
+      if (j == 0 && np1) {
+        t.seg = 0;
+        t.start = (n1 - 1) * BN;
+        t.cnt = ncache - t.start;
+      } else {
+        t.seg = 1;
+        t.start = (n2 - 1) * BN;
+        t.cnt = nq - t.start;
+      }
+    } else if (j < full1_end()) {
+      t.seg = 0;
+      t.start = (j - np1 - np2) * BN;
+      t.cnt = BN;
+    } else {
+      t.seg = 1;
+      t.start = (j - full1_end()) * BN;
+      t.cnt = BN;
+    }
+    return t;
+  }
+};
 
+template <int D, int NQB, int NW, bool KV8>
+struct Attn {
+  using G = Geo<D, NW>;
+  bf16x8 qf[NQB][D / 16];
   f32x16 O[NQB][D / 32];
   float m[NQB], l[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = -__builtin_inff();
-    l[qb] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) O[qb][e] = f32x16{};
+  int g, r32, s16, h16;
+  int kofs;        // K read: element offset of (row r32, chunk g), swizzled
+  int vlo, vhi;    // V transpose reads: offsets of the lane's rows kA and kA + 8 (u = 0, e = 0)
+  float c;
+
+  // With the row swizzle c -> c ^ f(row), chunk 2 s + g of row r sits at 8 ((2 s) ^
+  // (g ^ f(r))): the K read of step s is kofs ^ (16 s), and the V read of column block
+  // e is vlo ^ (32 e).  Row blocks (32 b, Ku) and the buffer are immediate offsets.
+  __device__ __forceinline__ void init_offsets(int lane) {
+    g = lane >> 5;
+    r32 = lane & 31;
+    s16 = lane & 15;
+    h16 = (lane >> 4) & 1;
+    kofs = swz_row_base<D>(r32, g);
+    const int kl = 4 * g + (s16 >> 2);
+    const int cl = 2 * h16 + ((s16 & 3) >> 1);
+    const int dhalf = 4 * (s16 & 1);
+    vlo = swz_row_base<D>(kl, cl) + dhalf;
+    vhi = swz_row_base<D>(kl + 8, cl) + dhalf;
   }
 
-  const int n1 = (p.ncache + BN - 1) / BN;
-  const int ntiles = n1 + (p.nq + BN - 1) / BN;
-  const float c = p.c;
-  const uint16_t* ck = KV8 ? nullptr : static_cast<const uint16_t*>(p.cK) + int64_t(h) * D;
-  const uint16_t* cv = KV8 ? nullptr : static_cast<const uint16_t*>(p.cV) + int64_t(h) * D;
-  const uint16_t* kc = p.Kc + int64_t(h) * D;
-  const uint16_t* vc = p.Vc + int64_t(h) * D;
-
-  Stage8<D> st8;
-  TileInfo ti = tile_info(0, n1, p.ncache, p.nq);
-  if (KV8 && ti.seg == 0) {
-    load_tile8<D>(st8, p, h, ti, tid);
-    store_tile8<D>(st8, sm_k[0], sm_v[0], sm_ks[0], sm_vs[0], tid);
-  } else {
-    dma_tile<D>(ti.seg == 0 ? ck : kc, ti.seg == 0 ? cv : vc, rs, ti, sm_k[0], sm_v[0], wave, lane);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const TileInfo cur = ti;
-    const bool more = j + 1 < ntiles;
-    bool next8 = false;
-    if (more) {
-      ti = tile_info(j + 1, n1, p.ncache, p.nq);
-      next8 = KV8 && ti.seg == 0;
-      if (next8) load_tile8<D>(st8, p, h, ti, tid);
-      else dma_tile<D>(ti.seg == 0 ? ck : kc, ti.seg == 0 ? cv : vc, rs, ti, sm_k[buf ^ 1], sm_v[buf ^ 1], wave, lane);
-    }
-    const uint16_t* lk = sm_k[buf];
-    const uint16_t* lv = sm_v[buf];
-
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks) ----
+  // One 64-key tile from LDS: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK: keys
+  // >= cnt are excluded; SCALED: int8 tile (scales from LDS) when `scaled` is set.
+  template <bool MASK, bool SCALED>
+  __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lks, const float* lvs,
+                                       int cnt, bool scaled = SCALED) {
     f32x16 S[NQB][2];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) S[qb][0] = S[qb][1] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const int ch = 2 * s + g;
-      const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + r32 * D + 8 * swz<D>(r32, ch)));
-      const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + (32 + r32) * D + 8 * swz<D>(32 + r32, ch)));
+      const int ko = kofs ^ (16 * s);
+      const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + ko));
+      const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + 32 * D + ko));
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         S[qb][0] = mfma32(k0, qf[qb][s], S[qb][0]);
         S[qb][1] = mfma32(k1, qf[qb][s], S[qb][1]);
       }
     }
-
-    const bool scaled = KV8 && cur.seg == 0;
-    if (scaled) {
+    if (SCALED && scaled) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 kscv = *reinterpret_cast<const f32x4*>(&sm_ks[KV8 ? buf : 0][32 * b + 8 * i + 4 * g]);
+          const f32x4 kscv = *reinterpret_cast<const f32x4*>(lks + 32 * b + 8 * i + 4 * g);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) S[qb][b][4 * i + jj] *= kscv[jj];
         }
     }
-    if (cur.cnt < BN) {
+    if (MASK) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            if (32 * b + 8 * i + 4 * g + jj >= cur.cnt) {
+          for (int jj = 0; jj < 4; ++jj)
+            if (32 * b + 8 * i + 4 * g + jj >= cnt) {
 #pragma unroll
               for (int qb = 0; qb < NQB; ++qb) S[qb][b][4 * i + jj] = -__builtin_inff();
             }
-          }
     }
 
-    // ---- online softmax (base 2, lazy rescale) ----
     bf16x8 P[NQB][4];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -303,12 +296,12 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p, int 
           S[qb][b][v] = e;
         }
       l[qb] += rsum;
-      if (scaled) {
+      if (SCALED && scaled) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const f32x4 vscv = *reinterpret_cast<const f32x4*>(&sm_vs[KV8 ? buf : 0][32 * b + 8 * i + 4 * g]);
+            const f32x4 vscv = *reinterpret_cast<const f32x4*>(lvs + 32 * b + 8 * i + 4 * g);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) S[qb][b][4 * i + jj] *= vscv[jj];
           }
@@ -325,42 +318,149 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p, int 
       }
     }
 
-    // ---- O^T += V^T P^T ----
-    // B slot t of step u holds key 32 (u>>1) + 16 (u&1) + 8 (t>>2) + 4 g + (t&3).  The
-    // transpose read gives lane s16 of a 16-lane group element (s16 & 3) of the rows
-    // addressed by lanes (s16 >> 2) + 4 k, k = 0..3: lane s16 therefore addresses key
-    // row kA + (s16 >> 2), columns d0 + 4 (s16 & 3) .. + 3.
+    // O^T += V^T P^T.  B slot t of step u holds key 32 (u>>1) + 16 (u&1) + 8 (t>>2) +
+    // 4 g + (t&3).  The transpose read gives lane s16 of a 16-lane group element
+    // (s16 & 3) of the rows addressed by lanes (s16 >> 2) + 4 k, k = 0..3: lane s16
+    // therefore addresses key row kA + (s16 >> 2), columns d0 + 4 (s16 & 3) .. + 3.
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) {
-      const int dcol = 32 * e + 16 * h16 + 4 * (s16 & 3);
-      const int dch = dcol >> 3, dhalf = dcol & 7;
+      const int olo = vlo ^ (32 * e), ohi = vhi ^ (32 * e);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int kA = 32 * (u >> 1) + 16 * (u & 1) + 4 * g + (s16 >> 2);
-        const int kB = kA + 8;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(lv + kA * D + 8 * swz<D>(kA, dch) + dhalf));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(lv + kB * D + 8 * swz<D>(kB, dch) + dhalf));
+        const int ku = (32 * (u >> 1) + 16 * (u & 1)) * D;   // row block: swizzle depends on row & 15 only
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + ku + olo));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + ku + ohi));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) O[qb][e] = mfma32(vf, P[qb][u], O[qb][e]);
       }
     }
+  }
+};
 
-    if (next8) {
-      store_tile8<D>(st8, sm_k[buf ^ 1], sm_v[buf ^ 1], sm_ks[KV8 ? buf ^ 1 : 0], sm_vs[KV8 ? buf ^ 1 : 0], tid);
+template <int D, int NQB, int NW, int MINB, bool KV8>
+__global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p, int n_qtiles, int n_blocks) {
+  using G = Geo<D, NW>;
+  // Two buffers per operand as separate LDS objects: the buffer parity is a compile-time
+  // constant at every access, which lets the compiler see that the copy into the next
+  // buffer does not alias the reads of the current one (no wait before the reads).
+  __shared__ __attribute__((aligned(1024))) uint16_t sm_k0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sm_k1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sm_v0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sm_v1[G::TILE];
+  __shared__ __attribute__((aligned(16))) float sm_ks0[KV8 ? BN : 1];
+  __shared__ __attribute__((aligned(16))) float sm_ks1[KV8 ? BN : 1];
+  __shared__ __attribute__((aligned(16))) float sm_vs0[KV8 ? BN : 1];
+  __shared__ __attribute__((aligned(16))) float sm_vs1[KV8 ? BN : 1];
+
+  // XCD-aware numbering: hardware deals block ids round-robin over the XCDs; give
+  // each XCD a contiguous range of logical blocks (query tiles of the same head).
+  const int per_xcd = (n_blocks + NXCD - 1) / NXCD;
+  const int bid = blockIdx.x;
+  const int logical = (bid % NXCD) * per_xcd + bid / NXCD;
+  if (logical >= n_blocks) return;
+  const int h = logical / n_qtiles;
+  const int qtile = logical % n_qtiles;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t rs = int64_t(p.H) * D;
+  const int q0 = qtile * (NW * 32 * NQB) + wave * (32 * NQB);
+
+  Attn<D, NQB, NW, KV8> A;
+  A.init_offsets(lane);
+  A.c = p.c;
+  // Q^T fragments (MFMA B operand): lane holds query r32, d = 16 s + 8 g + [0, 8)
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = q0 + 32 * qb + A.r32;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 w = {0, 0, 0, 0};
+      if (row < p.nq)
+        w = *reinterpret_cast<const u32x4*>(p.Q + int64_t(row) * rs + int64_t(h) * D + 16 * s + 8 * A.g);
+      A.qf[qb][s] = as_bf16x8(w);
     }
+    A.m[qb] = -__builtin_inff();
+    A.l[qb] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) A.O[qb][e] = f32x16{};
+  }
+
+  const TileOrder order(p.ncache, p.nq);
+  const int ntiles = order.total();
+  const uint16_t* ck = KV8 ? nullptr : static_cast<const uint16_t*>(p.cK) + int64_t(h) * D;
+  const uint16_t* cv = KV8 ? nullptr : static_cast<const uint16_t*>(p.cV) + int64_t(h) * D;
+  const uint16_t* kc = p.Kc + int64_t(h) * D;
+  const uint16_t* vc = p.Vc + int64_t(h) * D;
+
+  Stage8<D, NW> st8;
+  // Loads of tile j into buffer PB; int8 tiles land in registers (written by finish).
+  auto issue = [&](auto pb, int j) __attribute__((always_inline)) -> bool {
+    constexpr int PB = decltype(pb)::value;
+    uint16_t* lk = PB ? sm_k1 : sm_k0;
+    uint16_t* lv = PB ? sm_v1 : sm_v0;
+    const TileInfo t = order.at(j);
+    if (KV8 && t.seg == 0) {
+      load_tile8<D, NW>(st8, p, h, t, tid);
+      return true;
+    }
+    dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, lk, lv, wave, lane);
+    return false;
+  };
+  auto finish = [&](auto pb, bool pending) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pb)::value;
+    if (KV8 && pending)
+      store_tile8<D, NW>(st8, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, tid);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // Full tiles: prefetch the next tile into the other buffer, compute this one.  The
+  // buffer parity is a template argument so LDS accesses name a fixed buffer.
+  // KIND 1: int8 cache tiles (scaled), 2: bf16 tiles (cache or own chunk).
+  auto step = [&](auto pb, auto kind, int j) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pb)::value;
+    constexpr int KIND = decltype(kind)::value;
+    const bool pend = j + 1 < ntiles ? issue(std::integral_constant<int, PB ^ 1>{}, j + 1) : false;
+    A.template tile<false, KIND == 1>(PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_ks1 : sm_ks0,
+                                      PB ? sm_vs1 : sm_vs0, BN);
+    finish(std::integral_constant<int, PB ^ 1>{}, pend);
+  };
+  auto run = [&](auto kind, int j, int end) __attribute__((always_inline)) -> int {
+    if (j < end && (j & 1)) step(I1{}, kind, j++);
+    for (; j + 1 < end; j += 2) {
+      step(I0{}, kind, j);
+      step(I1{}, kind, j + 1);
+    }
+    if (j < end) step(I0{}, kind, j++);
+    return j;
+  };
+
+  finish(I0{}, issue(I0{}, 0));
+  int j = 0;
+  // Partial tiles (at most two): one generic masked path with run-time buffer choice.
+  for (; j < order.npart(); ++j) {
+    bool pend = false;
+    if (j + 1 < ntiles) pend = (j & 1) ? issue(I0{}, j + 1) : issue(I1{}, j + 1);
+    const TileInfo t = order.at(j);
+    const bool odd = j & 1;
+    A.template tile<true, KV8>(odd ? sm_k1 : sm_k0, odd ? sm_v1 : sm_v0, odd ? sm_ks1 : sm_ks0,
+                               odd ? sm_vs1 : sm_vs0, t.cnt, KV8 && t.seg == 0);
+    if (j & 1) finish(I0{}, pend);
+    else finish(I1{}, pend);
   }
+  if (KV8) j = run(std::integral_constant<int, 1>{}, j, order.full1_end());
+  run(std::integral_constant<int, 2>{}, j, ntiles);
 
   // ---- normalise and store O (lane: query r32, d = 32 e + 8 i + 4 g + [0, 4)) ----
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float lt = A.l[qb] + __shfl_xor(A.l[qb], 32);
     const float inv = 1.0f / lt;
-    const int row = q0 + 32 * qb + r32;
+    const int row = q0 + 32 * qb + A.r32;
     if (row < p.nq) {
       uint16_t* dst = p.out + int64_t(row) * rs + int64_t(h) * D;
 #pragma unroll
@@ -368,35 +468,43 @@ __global__ __launch_bounds__(NTHREADS) void attn_kernel(const AttnParams p, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           u32x2 w;
-          w.x = pack_bf16x2(O[qb][e][4 * i + 0] * inv, O[qb][e][4 * i + 1] * inv);
-          w.y = pack_bf16x2(O[qb][e][4 * i + 2] * inv, O[qb][e][4 * i + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + 32 * e + 8 * i + 4 * g) = w;
+          w.x = pack_bf16x2(A.O[qb][e][4 * i + 0] * inv, A.O[qb][e][4 * i + 1] * inv);
+          w.y = pack_bf16x2(A.O[qb][e][4 * i + 2] * inv, A.O[qb][e][4 * i + 3] * inv);
+          *reinterpret_cast<u32x2*>(dst + 32 * e + 8 * i + 4 * A.g) = w;
         }
     }
   }
 }
 
-template <int D, int NQB, bool KV8>
+template <int D, int NQB, int NW, bool KV8, int MINB = 1>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
-  const int rows = 4 * 32 * NQB;
+  const int rows = NW * 32 * NQB;
   const int n_qtiles = (p.nq + rows - 1) / rows;
   const int n_blocks = n_qtiles * p.H;
   const int grid = (n_blocks + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL((attn_kernel<D, NQB, KV8>), dim3(grid), dim3(NTHREADS), 0, s, p, n_qtiles, n_blocks);
+  hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KV8>), dim3(grid), dim3(64 * NW), 0, s, p, n_qtiles, n_blocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int D, bool kv_int8, hipStream_t s) {
+// 8 waves of 32 query rows: two waves per SIMD, so one wave's softmax overlaps the
+// other's MFMAs and every accumulator fits the 256 architected VGPRs.
+#ifndef LL_ATTN_NQB
+#define LL_ATTN_NQB 1
+#define LL_ATTN_NW 8
+#define LL_ATTN_MINB 1
+#endif
   const bool big = p.nq > 4 * 32;
   if (D == 128) {
-    if (kv_int8) return big ? launch_t<128, 2, true>(p, s) : launch_t<128, 1, true>(p, s);
-    return big ? launch_t<128, 2, false>(p, s) : launch_t<128, 1, false>(p, s);
+    if (kv_int8)
+      return big ? launch_t<128, LL_ATTN_NQB, LL_ATTN_NW, true, LL_ATTN_MINB>(p, s) : launch_t<128, 1, 4, true>(p, s);
+    return big ? launch_t<128, LL_ATTN_NQB, LL_ATTN_NW, false, LL_ATTN_MINB>(p, s) : launch_t<128, 1, 4, false>(p, s);
   }
   if (D == 64) {
-    if (kv_int8) return big ? launch_t<64, 2, true>(p, s) : launch_t<64, 1, true>(p, s);
-    return big ? launch_t<64, 2, false>(p, s) : launch_t<64, 1, false>(p, s);
+    if (kv_int8) return big ? launch_t<64, 2, 4, true>(p, s) : launch_t<64, 1, 4, true>(p, s);
+    return big ? launch_t<64, 2, 4, false>(p, s) : launch_t<64, 1, 4, false>(p, s);
   }
   return hipErrorInvalidValue;
 }
