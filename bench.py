@@ -198,6 +198,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the timed region, run a plain device copy of this many MiB "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the sink+window path runs "
@@ -213,6 +216,14 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
     ll.lib()   # no fallback: fail loudly without the HIP library
+
+    if args.calibration_copy_mib > 0:
+        src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = configs.STEADY
     r = run_steady(torch, ll, synth, cfg, args.steps, args.warmup)
