@@ -113,50 +113,55 @@ __device__ __forceinline__ void dma_tile(const uint16_t* gk, const uint16_t* gv,
   }
 }
 
+// int8 cache tile: each wave copies whole rows of raw codes into a staging area
+// (load-to-LDS, natural [row][D bytes] layout) and, after its own copies have landed,
+// widens exactly those rows to bf16 in the swizzled tile buffer (exact for |q| <= 127).
+// No wave reads another wave's staging rows, so no barrier is needed in between.  The
+// per-row scales are copied straight into their LDS arrays by waves 0 (K) and 1 (V).
 template <int D, int NW>
-struct Stage8 {
-  u32x2 k[Geo<D, NW>::REG_PASS];
-  u32x2 v[Geo<D, NW>::REG_PASS];
-  float sc;
+struct Int8Tile {
+  static constexpr int CH8 = D / 16;                 // 16-byte chunks per int8 row
+  static constexpr int ROWS = 64 / CH8;              // rows per wave-wide 1 KB copy
+  static constexpr int COPIES = BN / ROWS;           // copies per operand per tile
+  static constexpr int STAGE = BN * D;               // bytes per operand
+
+  __device__ static void issue(const AttnParams& p, int h, const TileInfo& ti, int8_t* stage, float* lks,
+                               float* lvs, int wave, int lane) {
+    const int64_t rs = int64_t(p.H) * D;
+    const int8_t* gk = static_cast<const int8_t*>(p.cK) + int64_t(h) * D;
+    const int8_t* gv = static_cast<const int8_t*>(p.cV) + int64_t(h) * D;
+    for (int i = wave; i < COPIES; i += NW) {
+      const int r0 = i * ROWS;
+      const int r = r0 + lane / CH8;
+      const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 16 * (lane % CH8);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gk + off), (lds_void*)(stage + r0 * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(gv + off), (lds_void*)(stage + STAGE + r0 * D), 16, 0, 0);
+    }
+    if (wave < 2) {
+      const float* sp = wave == 0 ? p.cKs : p.cVs;
+      const int64_t row = int64_t(ti.start + min(lane, ti.cnt - 1));
+      __builtin_amdgcn_global_load_lds((gbl_void*)(sp + row * p.H + h), (lds_void*)(wave == 0 ? lks : lvs), 4, 0,
+                                       0);
+    }
+  }
+
+  // Called by the same wave after s_waitcnt vmcnt(0).
+  __device__ static void widen(const int8_t* stage, uint16_t* lk, uint16_t* lv, int wave, int lane) {
+    for (int i = wave; i < COPIES; i += NW) {
+      const int r = i * ROWS + lane / CH8;
+      const int c16 = lane % CH8;
+#pragma unroll
+      for (int op = 0; op < 2; ++op) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(stage + op * STAGE + i * ROWS * D + 16 * lane);
+        uint16_t* dst = op ? lv : lk;
+        *reinterpret_cast<u32x4*>(dst + r * D + 8 * swz<D>(r, 2 * c16)) =
+            u32x4{i8x2_to_bf16x2(q.x, 0), i8x2_to_bf16x2(q.x, 2), i8x2_to_bf16x2(q.y, 0), i8x2_to_bf16x2(q.y, 2)};
+        *reinterpret_cast<u32x4*>(dst + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
+            u32x4{i8x2_to_bf16x2(q.z, 0), i8x2_to_bf16x2(q.z, 2), i8x2_to_bf16x2(q.w, 0), i8x2_to_bf16x2(q.w, 2)};
+      }
+    }
+  }
 };
-
-template <int D, int NW>
-__device__ __forceinline__ void load_tile8(Stage8<D, NW>& st, const AttnParams& p, int h, const TileInfo& ti,
-                                           int tid) {
-  using G = Geo<D, NW>;
-  const int64_t rs = int64_t(p.H) * D;
-  const int8_t* gk = static_cast<const int8_t*>(p.cK) + int64_t(h) * D;
-  const int8_t* gv = static_cast<const int8_t*>(p.cV) + int64_t(h) * D;
-#pragma unroll
-  for (int i = 0; i < G::REG_PASS; ++i) {
-    const int r = tid / G::CH + (G::NT / G::CH) * i;
-    const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 8 * (tid % G::CH);
-    st.k[i] = *reinterpret_cast<const u32x2*>(gk + off);
-    st.v[i] = *reinterpret_cast<const u32x2*>(gv + off);
-  }
-  st.sc = 0.0f;
-  if (tid < 2 * BN) {
-    const int r = tid % BN;
-    const float* sp = tid < BN ? p.cKs : p.cVs;
-    st.sc = r < ti.cnt ? sp[int64_t(ti.start + r) * p.H + h] : 0.0f;
-  }
-}
-
-template <int D, int NW>
-__device__ __forceinline__ void store_tile8(const Stage8<D, NW>& st, uint16_t* lk, uint16_t* lv, float* lks,
-                                            float* lvs, int tid) {
-  using G = Geo<D, NW>;
-#pragma unroll
-  for (int i = 0; i < G::REG_PASS; ++i) {
-    const int r = tid / G::CH + (G::NT / G::CH) * i;
-    const int pos = r * D + 8 * swz<D>(r, tid % G::CH);
-    *reinterpret_cast<u32x4*>(lk + pos) = u32x4{i8x2_to_bf16x2(st.k[i].x, 0), i8x2_to_bf16x2(st.k[i].x, 2),
-                                                i8x2_to_bf16x2(st.k[i].y, 0), i8x2_to_bf16x2(st.k[i].y, 2)};
-    *reinterpret_cast<u32x4*>(lv + pos) = u32x4{i8x2_to_bf16x2(st.v[i].x, 0), i8x2_to_bf16x2(st.v[i].x, 2),
-                                                i8x2_to_bf16x2(st.v[i].y, 0), i8x2_to_bf16x2(st.v[i].y, 2)};
-  }
-  if (tid < 2 * BN) (tid < BN ? lks : lvs)[tid % BN] = st.sc;
-}
 
 // Order of the key tiles: the (at most two) partial tiles -- the last tile of each
 // segment -- come first, so that the long run of full tiles after them carries no
@@ -224,12 +229,11 @@ struct Attn {
     vhi = swz_row_base<D>(kl + 8, cl) + dhalf;
   }
 
-  // One 64-key tile from LDS: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK: keys
-  // >= cnt are excluded; SCALED: int8 tile (scales from LDS) when `scaled` is set.
+  // S^T = K Q^T for the 64 keys of a tile (two 32-key blocks).  MASK: keys >= cnt get
+  // -inf; SCALED (int8 tile, when `scaled`): the per-key K scale multiplies its column.
   template <bool MASK, bool SCALED>
-  __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lks, const float* lvs,
-                                       int cnt, bool scaled = SCALED) {
-    f32x16 S[NQB][2];
+  __device__ __forceinline__ void scores(const uint16_t* lk, const float* lks, int cnt, bool scaled,
+                                         f32x16 (&S)[NQB][2]) const {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) S[qb][0] = S[qb][1] = f32x16{};
 #pragma unroll
@@ -267,8 +271,13 @@ struct Attn {
               for (int qb = 0; qb < NQB; ++qb) S[qb][b][4 * i + jj] = -__builtin_inff();
             }
     }
+  }
 
-    bf16x8 P[NQB][4];
+  // Online softmax of one tile (base 2, lazy rescale) -> bf16 probabilities in the
+  // B-operand layout of the P*V product.  SCALED: the per-key V scale multiplies P.
+  template <bool SCALED>
+  __device__ __forceinline__ void softmax(f32x16 (&S)[NQB][2], const float* lvs, bool scaled,
+                                          bf16x8 (&P)[NQB][4]) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       float mx = S[qb][0][0];
@@ -317,23 +326,81 @@ struct Attn {
         P[qb][u] = as_bf16x8(w);
       }
     }
+  }
 
-    // O^T += V^T P^T.  B slot t of step u holds key 32 (u>>1) + 16 (u&1) + 8 (t>>2) +
-    // 4 g + (t&3).  The transpose read gives lane s16 of a 16-lane group element
-    // (s16 & 3) of the rows addressed by lanes (s16 >> 2) + 4 k, k = 0..3: lane s16
-    // therefore addresses key row kA + (s16 >> 2), columns d0 + 4 (s16 & 3) .. + 3.
+  // V^T operand of column block e, step u.  B slot t of step u holds key 32 (u>>1) +
+  // 16 (u&1) + 8 (t>>2) + 4 g + (t&3).  The transpose read gives lane s16 of a 16-lane
+  // group element (s16 & 3) of the rows addressed by lanes (s16 >> 2) + 4 k, k = 0..3:
+  // lane s16 therefore addresses key row kA + (s16 >> 2), columns d0 + 4 (s16 & 3) .. + 3
+  // (the row swizzle depends on row & 15 only, so row blocks are immediate offsets).
+  __device__ __forceinline__ bf16x8 v_operand(const uint16_t* lv, int e, int u) const {
+    const int ku = (32 * (u >> 1) + 16 * (u & 1)) * D;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + ku + (vlo ^ (32 * e))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + ku + (vhi ^ (32 * e))));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // O^T += V^T P^T over the 64 keys of a tile.
+  __device__ __forceinline__ void pv(const uint16_t* lv, const bf16x8 (&P)[NQB][4]) {
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e) {
-      const int olo = vlo ^ (32 * e), ohi = vhi ^ (32 * e);
+    for (int e = 0; e < D / 32; ++e)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int ku = (32 * (u >> 1) + 16 * (u & 1)) * D;   // row block: swizzle depends on row & 15 only
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + ku + olo));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lv + ku + ohi));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 vf = v_operand(lv, e, u);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) O[qb][e] = mfma32(vf, P[qb][u], O[qb][e]);
       }
+  }
+
+  // One whole tile from LDS: scores, softmax, P*V.
+  template <bool MASK, bool SCALED>
+  __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lks, const float* lvs,
+                                       int cnt, bool scaled = SCALED) {
+    f32x16 S[NQB][2];
+    bf16x8 P[NQB][4];
+    scores<MASK, SCALED>(lk, lks, cnt, scaled, S);
+    softmax<SCALED>(S, lvs, scaled, P);
+    pv(lv, P);
+  }
+
+  // Normalise and store O (lane: query r32, d = 32 e + 8 i + 4 g + [0, 4)).
+  __device__ __forceinline__ void store(uint16_t* out, int q0, int nq, int64_t rs, int h) const {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = l[qb] + __shfl_xor(l[qb], 32);
+      const float inv = 1.0f / lt;
+      const int row = q0 + 32 * qb + r32;
+      if (row < nq) {
+        uint16_t* dst = out + int64_t(row) * rs + int64_t(h) * D;
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u32x2 w;
+            w.x = pack_bf16x2(O[qb][e][4 * i + 0] * inv, O[qb][e][4 * i + 1] * inv);
+            w.y = pack_bf16x2(O[qb][e][4 * i + 2] * inv, O[qb][e][4 * i + 3] * inv);
+            *reinterpret_cast<u32x2*>(dst + 32 * e + 8 * i + 4 * g) = w;
+          }
+      }
+    }
+  }
+
+  // Q^T fragments (MFMA B operand): lane holds query r32, d = 16 s + 8 g + [0, 8).
+  __device__ __forceinline__ void load_q(const uint16_t* Q, int q0, int nq, int64_t rs, int h, float c_) {
+    c = c_;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = q0 + 32 * qb + r32;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        u32x4 w = {0, 0, 0, 0};
+        if (row < nq) w = *reinterpret_cast<const u32x4*>(Q + int64_t(row) * rs + int64_t(h) * D + 16 * s + 8 * g);
+        qf[qb][s] = as_bf16x8(w);
+      }
+      m[qb] = -__builtin_inff();
+      l[qb] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) O[qb][e] = f32x16{};
     }
   }
 };
@@ -352,6 +419,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   __shared__ __attribute__((aligned(16))) float sm_ks1[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(16))) float sm_vs0[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(16))) float sm_vs1[KV8 ? BN : 1];
+  __shared__ __attribute__((aligned(1024))) int8_t sm_stage[KV8 ? 2 * Int8Tile<D, NW>::STAGE : 16];
 
   // XCD-aware numbering: hardware deals block ids round-robin over the XCDs; give
   // each XCD a contiguous range of logical blocks (query tiles of the same head).
@@ -370,23 +438,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
 
   Attn<D, NQB, NW, KV8> A;
   A.init_offsets(lane);
-  A.c = p.c;
-  // Q^T fragments (MFMA B operand): lane holds query r32, d = 16 s + 8 g + [0, 8)
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = q0 + 32 * qb + A.r32;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 w = {0, 0, 0, 0};
-      if (row < p.nq)
-        w = *reinterpret_cast<const u32x4*>(p.Q + int64_t(row) * rs + int64_t(h) * D + 16 * s + 8 * A.g);
-      A.qf[qb][s] = as_bf16x8(w);
-    }
-    A.m[qb] = -__builtin_inff();
-    A.l[qb] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) A.O[qb][e] = f32x16{};
-  }
+  A.load_q(p.Q, q0, p.nq, rs, h, p.c);
 
   const TileOrder order(p.ncache, p.nq);
   const int ntiles = order.total();
@@ -395,25 +447,23 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   const uint16_t* kc = p.Kc + int64_t(h) * D;
   const uint16_t* vc = p.Vc + int64_t(h) * D;
 
-  Stage8<D, NW> st8;
-  // Loads of tile j into buffer PB; int8 tiles land in registers (written by finish).
+  // Loads of tile j into buffer PB.  int8 tiles go to the staging area first and are
+  // widened by finish().  Returns true when a widening is pending.
   auto issue = [&](auto pb, int j) __attribute__((always_inline)) -> bool {
     constexpr int PB = decltype(pb)::value;
-    uint16_t* lk = PB ? sm_k1 : sm_k0;
-    uint16_t* lv = PB ? sm_v1 : sm_v0;
     const TileInfo t = order.at(j);
     if (KV8 && t.seg == 0) {
-      load_tile8<D, NW>(st8, p, h, t, tid);
+      Int8Tile<D, NW>::issue(p, h, t, sm_stage, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, wave, lane);
       return true;
     }
-    dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, lk, lv, wave, lane);
+    dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0,
+                    wave, lane);
     return false;
   };
   auto finish = [&](auto pb, bool pending) __attribute__((always_inline)) {
     constexpr int PB = decltype(pb)::value;
-    if (KV8 && pending)
-      store_tile8<D, NW>(st8, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, tid);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (KV8 && pending) Int8Tile<D, NW>::widen(sm_stage, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, wave, lane);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
@@ -455,25 +505,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   if (KV8) j = run(std::integral_constant<int, 1>{}, j, order.full1_end());
   run(std::integral_constant<int, 2>{}, j, ntiles);
 
-  // ---- normalise and store O (lane: query r32, d = 32 e + 8 i + 4 g + [0, 4)) ----
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = A.l[qb] + __shfl_xor(A.l[qb], 32);
-    const float inv = 1.0f / lt;
-    const int row = q0 + 32 * qb + A.r32;
-    if (row < p.nq) {
-      uint16_t* dst = p.out + int64_t(row) * rs + int64_t(h) * D;
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x2 w;
-          w.x = pack_bf16x2(A.O[qb][e][4 * i + 0] * inv, A.O[qb][e][4 * i + 1] * inv);
-          w.y = pack_bf16x2(A.O[qb][e][4 * i + 2] * inv, A.O[qb][e][4 * i + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + 32 * e + 8 * i + 4 * A.g) = w;
-        }
-    }
-  }
+  A.store(p.out, q0, p.nq, rs, h);
 }
 
 template <int D, int NQB, int NW, bool KV8, int MINB = 1>
