@@ -10,7 +10,7 @@
 // slot, so this is a streaming 16-byte-vector copy (HBM bound).
 // int8 caches: each (token, head) row of D values is quantised on the fly
 //   a = max |x|, scale = a / 127, q = clamp(rint((x * 127) / a), -127, 127)
-// (every operation IEEE binary32, correctly rounded division, ties-to-even rounding;
+// (every operation IEEE binary32, correctly rounded quotient, ties-to-even rounding;
 // x * 127 is exact for bf16 x).  LongLive-2.0 explainer, wmrh.cn, §15.2: the history
 // cache is stored in low precision to save memory and traffic.
 #include "device_common.h"
@@ -42,47 +42,76 @@ __global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams
   }
 }
 
-// One (token, head) row of D values per LPR = D / 8 lanes; each lane owns 8 values.
+// One (token, head) row of D values per LPR = D / 8 lanes; each lane owns 8 values of
+// RPG rows, whose loads are all issued before any arithmetic (bytes in flight).
+//
+// Division: q = rint(n / a) with n = x * 127 needs the correctly rounded quotient.  With
+// y = RN(1/a) (one IEEE division per row) and q0 = RN(n * y) within one ulp of n/a, the
+// residual r = n - a * q0 is exact as one FMA and RN(q0 + r * y) is the correctly rounded
+// n/a (Markstein's theorem for floating-point division, e.g. J.-M. Muller et al.,
+// Handbook of Floating-Point Arithmetic, ch. on division).  It needs no underflow or
+// overflow, so rows whose absmax is below 2^-100 or above 2^120 (where x * 127 may
+// overflow) use the plain IEEE division.
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParams p) {
   constexpr int LPR = D / 8;
-  constexpr int ROWS_PER_BLOCK = kThreads / LPR;
+  constexpr int GROUPS = kThreads / LPR;
+  constexpr int RPG = 4;
   const int e = blockIdx.y;
   const bool isv = blockIdx.z != 0;
-  const int64_t row_in_frame = int64_t(blockIdx.x) * ROWS_PER_BLOCK + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
-  const bool active = row_in_frame < p.rows_per_frame;
-  const int64_t src_row = int64_t(p.plan_src[e]) * p.rows_per_frame + row_in_frame;
-  const int64_t dst_row = int64_t(p.plan_slot[e]) * p.rows_per_frame + row_in_frame;
+  const int64_t row0 = (int64_t(blockIdx.x) * GROUPS + threadIdx.x / LPR) * RPG;
+  const uint16_t* src = (isv ? p.srcV : p.srcK) + int64_t(p.plan_src[e]) * p.rows_per_frame * D;
+  int8_t* dst = static_cast<int8_t*>(isv ? p.dstV : p.dstK) + int64_t(p.plan_slot[e]) * p.rows_per_frame * D;
+  float* dsc = (isv ? p.dstVs : p.dstKs) + int64_t(p.plan_slot[e]) * p.rows_per_frame;
 
-  u32x4 w = {0, 0, 0, 0};
-  if (active) w = *reinterpret_cast<const u32x4*>((isv ? p.srcV : p.srcK) + src_row * D + 8 * sub);
-  float x[8];
+  u32x4 w[RPG];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
-    x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+  for (int rr = 0; rr < RPG; ++rr) {
+    const int64_t row = row0 + rr;
+    w[rr] = row < p.rows_per_frame ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * D + 8 * sub))
+                                   : u32x4{0, 0, 0, 0};
   }
-  float a = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
+  for (int rr = 0; rr < RPG; ++rr) {
+    const int64_t row = row0 + rr;
+    float x[8];
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, LPR));
-
-  const float scale = a / 127.0f;
-  uint32_t packed[2] = {0u, 0u};
-  if (a > 0.0f) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float t = __builtin_rintf((x[k] * 127.0f) / a);
-      const int qi = int(fminf(fmaxf(t, -127.0f), 127.0f));
-      packed[k >> 2] |= (uint32_t(qi) & 0xffu) << (8 * (k & 3));
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __builtin_bit_cast(float, w[rr][k] << 16);
+      x[2 * k + 1] = __builtin_bit_cast(float, w[rr][k] & 0xffff0000u);
     }
-  }
-  if (active) {
-    int8_t* dst = static_cast<int8_t*>(isv ? p.dstV : p.dstK);
-    *reinterpret_cast<u32x2*>(dst + dst_row * D + 8 * sub) = u32x2{packed[0], packed[1]};
-    if (sub == 0) (isv ? p.dstVs : p.dstKs)[dst_row] = scale;
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, LPR));
+
+    const float scale = a / 127.0f;
+    uint32_t packed[2] = {0u, 0u};
+    if (a > 0.0f) {
+      const bool plain = a < 0x1p-100f || a > 0x1p+120f;
+      const float y = 1.0f / a;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float n = x[k] * 127.0f;   // exact for bf16 x
+        float qq;
+        if (plain) {
+          qq = n / a;
+        } else {
+          qq = n * y;
+          const float r = __builtin_fmaf(-a, qq, n);
+          qq = __builtin_fmaf(r, y, qq);
+        }
+        const float t = __builtin_rintf(qq);
+        const int qi = int(fminf(fmaxf(t, -127.0f), 127.0f));
+        packed[k >> 2] |= (uint32_t(qi) & 0xffu) << (8 * (k & 3));
+      }
+    }
+    if (row < p.rows_per_frame) {
+      *reinterpret_cast<u32x2*>(dst + row * D + 8 * sub) = u32x2{packed[0], packed[1]};
+      if (sub == 0) dsc[row] = scale;
+    }
   }
 }
 
@@ -97,7 +126,7 @@ hipError_t launch_kv_write(const WriteParams& p, int D, bool kv_int8, hipStream_
     hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kThreads), 0, s, p, vecs);
     return hipGetLastError();
   }
-  const int rows_per_block = kThreads / (D / 8);
+  const int rows_per_block = kThreads / (D / 8) * 4;
   dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
   if (D == 128) {
     hipLaunchKernelGGL(quant_frames_kernel<128>, grid, dim3(kThreads), 0, s, p);

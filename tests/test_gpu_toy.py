@@ -187,3 +187,40 @@ def test_empty_cache_first_chunk_and_ragged_lengths(torch_gpu):
             compare_attention(out, ref, f"T={T} chunk {k}")
             cache.append(0, synth.to_device(kc), synth.to_device(vc))
             hist.append(kc, vc)
+
+
+def test_int8_quantisation_edge_rows_bit_exact(torch_gpu):
+    """Rows built to hit every branch of the int8 rule: exact .5 ties, +-absmax, all-zero
+    rows, a single non-zero element, tiny (~2^-110) and huge (~2^121, x*127 overflows)
+    magnitudes, and ordinary Gaussian rows; codes and scales must equal the oracle's."""
+    T, H, D, S, W = 24, 2, 128, 2, 3
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((T, H, D)).astype(np.float32)
+    ties = np.zeros(D, dtype=np.float32)
+    ties[:8] = [254.0, 1.0, 3.0, 5.0, -1.0, -3.0, -5.0, -254.0]
+    ties[8:] = (2 * rng.integers(-60, 60, D - 8) + 1).astype(np.float32)
+    for t in range(T):
+        kind = t % 8
+        if kind == 1:
+            x[t] = 0.0
+        elif kind == 2:
+            x[t] = ties
+        elif kind == 3:
+            x[t] *= np.float32(2.0 ** -110)
+        elif kind == 4:
+            x[t] *= np.float32(2.0 ** 121)
+        elif kind == 5:
+            x[t] = 0.0
+            x[t, :, t % D] = -3.5
+        elif kind == 6:
+            x[t, 0] *= np.float32(2.0 ** -20)
+            x[t, 1] *= np.float32(2.0 ** 20)
+    frames = synth.f32_to_bf16_bits(x)
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8")
+    hist = History(S, W, T)
+    for k in range(4):
+        kb = frames if k % 2 == 0 else synth.f32_to_bf16_bits(-x)
+        vb = synth.f32_to_bf16_bits(x[::-1].copy())
+        cache.append(0, synth.to_device(kb), synth.to_device(vb))
+        hist.append(kb, vb)
+        check_slots(cache, 0, hist, kv_int8=True)
