@@ -156,6 +156,85 @@ def run_recache_layer(torch, ll, synth, cfg, reps=10):
             "rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS}
 
 
+def run_rollout(torch, ll, synth, cfg):
+    """Whole multi-layer rollout: per chunk, `passes` attention calls per layer, then one
+    append per layer (and the recache of every layer before chunks k*recache_every).
+    Inputs come from a pool of seeded device tensors made before timing."""
+    C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
+    shape = (cfg.nq, H, D)
+    cache = ll.Cache(cfg.layers, H, D, T, S, W, kv_dtype="int8" if cfg.kv_int8 else "bf16")
+    pool = [tuple(synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, t, 2000 + i) for t in range(3))
+            for i in range(POOL)]
+    n_re = S + W
+    rec = None
+    if cfg.recache_every:
+        rec = (synth.normal_bf16_device((n_re * T, H, D), cfg.sigma, cfg.seed, 30),
+               synth.normal_bf16_device((n_re * T, H, D), cfg.sigma, cfg.seed, 31))
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    flops = 0.0
+    t0 = time.perf_counter()
+    e0.record()
+    i = 0
+    for k in range(cfg.chunks):
+        if rec is not None and k > 0 and k % cfg.recache_every == 0:
+            for l in range(cfg.layers):
+                cache.recache(l, *rec)
+        n_vis = min(cache.frames_seen(0), S + W)
+        for p in range(cfg.passes):
+            for l in range(cfg.layers):
+                q, kk, vv = pool[i % POOL]
+                i += 1
+                cache.attn(l, q, kk, vv, out)
+        flops += cfg.passes * cfg.layers * _attn_flops(H, D, cfg.nq, (n_vis + C) * T)
+        for l in range(cfg.layers):
+            cache.append(l, kk, vv)
+        if k % 20 == 19:
+            print(f"# {cfg.name}: chunk {k + 1}/{cfg.chunks}", file=sys.stderr, flush=True)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = e0.elapsed_time(e1) / 1e3
+    frames = cfg.chunks * C
+    cache.close()
+    return {"workload": cfg.name, "layers": cfg.layers, "latent_frames": frames, "seconds": gpu_s, "wall_s": wall,
+            "latent_frames_per_s_stack": frames / gpu_s, "latent_frames_per_s_per_layer": frames * cfg.layers / gpu_s,
+            "attention_flop": flops, "avg_tflops_incl_append": flops / gpu_s / 1e12}
+
+
+def run_window_sweep(torch, ll, synth, base, steps=10):
+    """The pages' window/sink ablation as a kernel workload at the 1.3B shape: the
+    attention pass and the append of a steady-state chunk for window 21 without sink,
+    window 12 without sink and window 9 with a 3-frame sink, plus KV memory per layer."""
+    res = []
+    for S, W in ((0, 21), (0, 12), (3, 9)):
+        cfg = configs_mod().Workload(**{**base.__dict__, "sink": S, "window": W, "name": f"sweep_s{S}_w{W}"})
+        r = run_steady(torch, ll, synth, cfg, steps, 2)
+        kv_bytes = 2 * (S + W) * cfg.tokens_per_frame * cfg.heads * cfg.head_dim * 2
+        res.append({"sink": S, "window": W, "visible_keys": r["keys"], "attn_ms": r["attn_ms"],
+                    "attn_tflops": r["attn_tflops"], "append_us": r["append_us"],
+                    "step_ms": r["wall_s"] / steps * 1e3, "kv_bytes_per_layer": kv_bytes})
+    ref = res[0]
+    for r in res:
+        r["step_time_vs_w21"] = r["step_ms"] / ref["step_ms"] - 1.0
+        r["kv_memory_vs_w21"] = r["kv_bytes_per_layer"] / ref["kv_bytes_per_layer"] - 1.0
+    return res
+
+
+def run_recache_stack(torch, ll, synth, cfg, reps=3):
+    """Recache of every layer: projection then rewrite per layer, then the next chunk's
+    attention on every layer (the prompt-switch workload)."""
+    r = run_recache_layer(torch, ll, synth, cfg, reps=reps)
+    stack_ms = cfg.layers * (r["proj_ms"] + r["rewrite_us"] / 1e3)
+    return {"workload": cfg.name, "layers": cfg.layers, "per_layer": r, "stack_ms_projection_plus_rewrite": stack_ms}
+
+
+def configs_mod():
+    from synth import configs
+    return configs
+
+
 def cpu_baseline(cfg):
     """The CPU oracle as it stands, on one full steady-state step (4 passes over all
     4680 query rows x 12 heads, then the append bookkeeping), on this host."""
@@ -198,6 +277,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--workload", default="steady", choices=["steady", "rollout", "long_int8", "recache", "sweep"],
+                    help="steady (default): the one-chunk step below; the others print their own "
+                         "JSON record: 30-layer rollout, 400-chunk int8 rollout with recache, "
+                         "30-layer recache, window/sink sweep")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -224,6 +307,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.workload != "steady":
+        if args.workload == "rollout":
+            rec = run_rollout(torch, ll, synth, configs.ROLLOUT)
+        elif args.workload == "long_int8":
+            rec = run_rollout(torch, ll, synth, configs.LONG_INT8)
+        elif args.workload == "recache":
+            rec = run_recache_stack(torch, ll, synth, configs.RECACHE)
+        else:
+            rec = {"workload": "window_sink_sweep", "rows": run_window_sweep(torch, ll, synth, configs.STEADY)}
+        print(json.dumps(rec), flush=True)
+        return
 
     cfg = configs.STEADY
     r = run_steady(torch, ll, synth, cfg, args.steps, args.warmup)
