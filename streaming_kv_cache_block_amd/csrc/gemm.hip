@@ -6,29 +6,71 @@
 // retained latents under the new prompt.  W is the [d_out][d_in] matrix of that
 // column form, so both operands are contiguous along the contraction d_in.
 //
-// Tiling: a workgroup of 4 waves computes 256 tokens x 128 outputs; each wave
-// 128 tokens x 64 outputs with 32x32x16 bf16 MFMAs (W rows as the A operand, h rows
-// as the B operand, so a lane's accumulators hold 4 consecutive outputs of one token
-// and the bf16 results leave as 8-byte stores).  The contraction is walked in steps
-// of 64 through double-buffered LDS fed by register prefetch.  blockIdx.z selects
-// the K or the V projection, so both come from one launch.
+// Tiling: a workgroup of 4 waves computes 256 tokens x 128 outputs; each wave 128
+// tokens x 64 outputs with 32x32x16 bf16 MFMAs (W rows as the A operand, h rows as
+// the B operand, so a lane's accumulators hold 4 consecutive outputs of one token and
+// the bf16 results leave as 8-byte stores).  The contraction is walked in steps of 32:
+// each step's h and W tiles are copied global -> LDS with the load-to-LDS path into
+// two buffers that are separate LDS objects (buffer parity fixed at compile time, so
+// the copy of step s+1 overlaps the MFMAs of step s).  Within a 64-byte row the four
+// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, which makes the 16 rows that one
+// operand read touches land on 16 distinct bank groups.  48 KB of LDS and <= 256
+// registers let two workgroups share a CU (two waves per SIMD).  blockIdx.z selects
+// the K or V projection, and workgroups that share an h tile run on the same XCD.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace ll {
 namespace {
 
-constexpr int TM = 256;     // tokens per workgroup
-constexpr int TN = 128;     // outputs per workgroup
-constexpr int TK = 64;      // contraction step
-constexpr int PITCH = TK + 8;
+constexpr int TM = 256;      // tokens per workgroup
+constexpr int TN = 128;      // outputs per workgroup
+constexpr int TK = 32;       // contraction step
 constexpr int NT = 256;
-constexpr int HPASS = TM * (TK / 8) / NT;   // 16-byte h chunks per thread per step (8)
-constexpr int WPASS = TN * (TK / 8) / NT;   // 16-byte W chunks per thread per step (4)
+constexpr int NXCD = 8;
+constexpr int HCOPY = TM * TK * 2 / 1024;   // 1 KB wave-wide copies of the h tile (16)
+constexpr int WCOPY = TN * TK * 2 / 1024;   // of the W tile (8)
 
-__global__ __launch_bounds__(NT) void proj_kernel(const ProjParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sh[2][TM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sw[2][TN * PITCH];
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// element offset of 16-byte chunk c (0..3) of row r in a swizzled [rows][TK] tile
+__device__ __forceinline__ int gswz(int r, int c) { return r * TK + 8 * (c ^ ((r >> 2) & 3)); }
+
+// Copy rows [0, rows) x [k0, k0 + TK) of a row-major [*, ld] bf16 matrix into LDS.
+// Lane l of copy i fills LDS bytes [1 KB i + 16 l, +16): row 16 i + l / 4, chunk
+// position l % 4, which holds source chunk (l % 4) ^ ((row >> 2) & 3).
+template <int NCOPY>
+__device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t ld, int row0, int rows_valid, int k0,
+                                          uint16_t* lds, int wave, int lane) {
+#pragma unroll
+  for (int i = wave; i < NCOPY; i += 4) {
+    const int r = 16 * i + lane / 4;
+    const int c = (lane % 4) ^ ((r >> 2) & 3);
+    const int rr = min(r, rows_valid - 1);
+    __builtin_amdgcn_global_load_lds((gbl_void*)(g + int64_t(row0 + rr) * ld + k0 + 8 * c),
+                                     (lds_void*)(lds + 16 * i * TK), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(NT, 2) void proj_kernel(const ProjParams p, int n_mt, int n_units) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sh0[TM * TK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sh1[TM * TK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sw0[TN * TK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sw1[TN * TK];
+
+  // logical unit = (token tile, output tile, K/V); the units of one token tile are
+  // consecutive and each XCD gets a contiguous range of units.
+  const int per_xcd = (n_units + NXCD - 1) / NXCD;
+  const int logical = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  if (logical >= n_units) return;
+  const int n_nt = p.N / TN;
+  const int mt = logical / (2 * n_nt);
+  const int rem = logical % (2 * n_nt);
+  const int nt = rem >> 1;
+  const int z = rem & 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -37,33 +79,11 @@ __global__ __launch_bounds__(NT) void proj_kernel(const ProjParams p) {
   const int r32 = lane & 31;
   const int wm = wave & 1;     // token half
   const int wn = wave >> 1;    // output half
-  const int m0 = blockIdx.x * TM;
-  const int n0 = blockIdx.y * TN;
-  const uint16_t* W = blockIdx.z ? p.WV : p.WK;
-  uint16_t* out = blockIdx.z ? p.outV : p.outK;
-
-  const int c = tid % 8;       // 16-byte chunk within a 64-element row
-  const int rb = tid / 8;      // 0..31
-
-  u32x4 ph[HPASS], pw[WPASS];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < HPASS; ++i) {
-      const int row = m0 + rb + 32 * i;
-      ph[i] = row < p.M ? *reinterpret_cast<const u32x4*>(p.h + int64_t(row) * p.K + k0 + 8 * c) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < WPASS; ++i) {
-      const int row = n0 + rb + 32 * i;
-      pw[i] = *reinterpret_cast<const u32x4*>(W + int64_t(row) * p.K + k0 + 8 * c);
-    }
-  };
-  auto store = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < HPASS; ++i) *reinterpret_cast<u32x4*>(&sh[b][(rb + 32 * i) * PITCH + 8 * c]) = ph[i];
-#pragma unroll
-    for (int i = 0; i < WPASS; ++i) *reinterpret_cast<u32x4*>(&sw[b][(rb + 32 * i) * PITCH + 8 * c]) = pw[i];
-  };
+  const int m0 = mt * TM;
+  const int n0 = nt * TN;
+  const int m_valid = min(TM, p.M - m0);
+  const uint16_t* W = z ? p.WV : p.WK;
+  uint16_t* out = z ? p.outV : p.outK;
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -71,33 +91,48 @@ __global__ __launch_bounds__(NT) void proj_kernel(const ProjParams p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-  const int nsteps = p.K / TK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < nsteps;
-    if (more) load((st + 1) * TK);
-    const uint16_t* hs = sh[buf];
-    const uint16_t* ws = sw[buf];
+  auto issue = [&](auto pb, int k0) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pb)::value;
+    copy_tile<HCOPY>(p.h, p.K, m0, m_valid, k0, PB ? sh1 : sh0, wave, lane);
+    copy_tile<WCOPY>(W, p.K, n0, TN, k0, PB ? sw1 : sw0, wave, lane);
+  };
+  auto compute = [&](auto pb) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pb)::value;
+    const uint16_t* hs = PB ? sh1 : sh0;
+    const uint16_t* ws = PB ? sw1 : sw0;
 #pragma unroll
     for (int kk = 0; kk < TK / 16; ++kk) {
       bf16x8 af[2], bfr[4];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
-        af[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(ws + (64 * wn + 32 * a + r32) * PITCH + 16 * kk + 8 * g));
+        af[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(ws + gswz(64 * wn + 32 * a + r32, 2 * kk + g)));
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        bfr[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(hs + (128 * wm + 32 * b + r32) * PITCH + 16 * kk + 8 * g));
+        bfr[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(hs + gswz(128 * wm + 32 * b + r32, 2 * kk + g)));
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
     }
-    if (more) store(buf ^ 1);
+  };
+  auto step = [&](auto pb, int st, int nsteps) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pb)::value;
+    if (st + 1 < nsteps) issue(std::integral_constant<int, PB ^ 1>{}, (st + 1) * TK);
+    compute(pb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  const int nsteps = p.K / TK;
+  issue(std::integral_constant<int, 0>{}, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(std::integral_constant<int, 0>{}, st, nsteps);
+    step(std::integral_constant<int, 1>{}, st + 1, nsteps);
   }
+  if (st < nsteps) step(std::integral_constant<int, 0>{}, st, nsteps);
 
   // lane: token 128 wm + 32 b + r32, outputs 64 wn + 32 a + 8 i + 4 g + [0, 4)
 #pragma unroll
@@ -121,8 +156,10 @@ __global__ __launch_bounds__(NT) void proj_kernel(const ProjParams p) {
 
 hipError_t launch_kv_project(const ProjParams& p, hipStream_t s) {
   if (p.K % TK != 0 || p.N % TN != 0 || p.M <= 0) return hipErrorInvalidValue;
-  dim3 grid(unsigned((p.M + TM - 1) / TM), unsigned(p.N / TN), 2);
-  hipLaunchKernelGGL(proj_kernel, grid, dim3(NT), 0, s, p);
+  const int n_mt = (p.M + TM - 1) / TM;
+  const int n_units = n_mt * (p.N / TN) * 2;
+  const int grid = (n_units + NXCD - 1) / NXCD * NXCD;
+  hipLaunchKernelGGL(proj_kernel, dim3(grid), dim3(NT), 0, s, p, n_mt, n_units);
   return hipGetLastError();
 }
 
