@@ -141,3 +141,32 @@ def test_recache_projection_then_rewrite_then_attention(torch_gpu):
     rows = sample_rows(cfg.nq, T, seed=3)
     ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, rows=rows)
     compare_attention(synth.to_bits(out)[rows], ref, "attention after recache")
+
+
+def test_frame_id_probe_at_full_shape(torch_gpu):
+    """Frame-id probe at the 1.3B shape (12 heads x 128, 1560 tokens per frame, wrapped
+    ring): K = 0 and V one-hot at d = frame id make every probability 1, so the output
+    must be exactly (#visible tokens of frame d) / (#visible tokens)."""
+    torch = torch_gpu
+    from oracle import visibility
+    T, H, D, S, W, C = 1560, 12, 128, 3, 12, 3
+    cache = ll.Cache(1, H, D, T, S, W)
+    f0 = 0
+    for k in range(12):
+        kz = torch.zeros((C * T, H, D), device="cuda", dtype=torch.bfloat16)
+        v = torch.zeros((C * T, H, D), device="cuda", dtype=torch.bfloat16)
+        for i in range(C):
+            v[i * T:(i + 1) * T, :, (f0 + i) % D] = 1.0
+        if k >= 5:
+            q = synth.normal_bf16_device((C * T, H, D), 0.5, 77, k)
+            out = cache.attn(0, q, kz, v)
+            vis = visibility.visible_frames(f0, C, S, W)
+            expect = np.zeros(D)
+            for f in vis:
+                expect[f % D] += T
+            expect /= len(vis) * T
+            got = bf16.to_f32(synth.to_bits(out)).astype(np.float64)
+            want = bf16.to_f32(bf16.round_f32(expect.astype(np.float32))).astype(np.float64)
+            assert np.abs(got - want[None, None, :]).max() <= np.abs(want).max() * 2 ** -7, (k, f0)
+        cache.append(0, kz, v)
+        f0 += C
