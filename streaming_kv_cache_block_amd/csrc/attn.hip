@@ -340,12 +340,13 @@ struct Attn {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // O^T += V^T P^T over the 64 keys of a tile.
+  // O^T += V^T P^T over the 64 keys of a tile.  Key-step-major: the first MFMAs need
+  // only the first 8 probabilities, so they can start while later exps are computed.
   __device__ __forceinline__ void pv(const uint16_t* lv, const bf16x8 (&P)[NQB][4]) {
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int e = 0; e < D / 32; ++e) {
         const bf16x8 vf = v_operand(lv, e, u);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) O[qb][e] = mfma32(vf, P[qb][u], O[qb][e]);
