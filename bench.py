@@ -122,38 +122,59 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False):
 
 
 def run_recache_layer(torch, ll, synth, cfg, reps=10):
-    """Projection GEMM and rewrite of one layer at the recache workload's size."""
+    """Recache of one layer at the recache workload's size, bf16 and int8 caches:
+    projection GEMM then rewrite (two launches, K/V round trip through HBM), and the
+    fused projection whose epilogue writes the slots."""
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     hid = cfg.hidden
-    cache = ll.Cache(1, H, D, T, S, W)
     shape = (cfg.nq, H, D)
-    for k in range(cfg.prefill_chunks):
-        cache.append(0, synth.normal_bf16_device(shape, 1.0, cfg.seed, 1, k),
-                     synth.normal_bf16_device(shape, 1.0, cfg.seed, 2, k))
-    n = min(cache.frames_seen(0), S + W)
-    h = synth.normal_bf16_device((n * T, hid), 1.0, cfg.seed, 10, 0)
-    wk = synth.normal_bf16_device((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 11, 0)
-    wv = synth.normal_bf16_device((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 12, 0)
-    K, V = ll.kv_project(h, wk, wv)
-    cache.recache(0, K, V)
-    torch.cuda.synchronize()
-    g0, g1, r0, r1 = (_events(torch, reps) for _ in range(4))
-    for i in range(reps):
-        g0[i].record()
-        ll.kv_project(h, wk, wv, K, V)
-        g1[i].record()
-        r0[i].record()
+    res = {}
+    for kv in ("bf16", "int8"):
+        cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
+        for k in range(cfg.prefill_chunks):
+            cache.append(0, synth.normal_bf16_device(shape, 1.0, cfg.seed, 1, k),
+                         synth.normal_bf16_device(shape, 1.0, cfg.seed, 2, k))
+        n = min(cache.frames_seen(0), S + W)
+        h = synth.normal_bf16_device((n * T, hid), 1.0, cfg.seed, 10, 0)
+        wk = synth.normal_bf16_device((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 11, 0)
+        wv = synth.normal_bf16_device((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 12, 0)
+        K, V = ll.kv_project(h, wk, wv)
         cache.recache(0, K, V)
-        r1[i].record()
-    torch.cuda.synchronize()
-    gms = sum(g0[i].elapsed_time(g1[i]) for i in range(reps)) / reps
-    rms = sum(r0[i].elapsed_time(r1[i]) for i in range(reps)) / reps
-    flops = 2.0 * 2 * n * T * hid * hid
-    rbytes = 2 * 2 * n * T * H * D * 2
-    cache.close()
-    return {"proj_ms": gms, "proj_tflops": flops / gms / 1e9, "proj_frac": flops / gms / 1e9 / PEAK_BF16_TFLOPS,
-            "rewrite_us": rms * 1e3, "rewrite_bytes": rbytes, "rewrite_gbs": rbytes / rms / 1e6,
-            "rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS}
+        cache.recache_from_hidden(0, h, wk, wv)
+        torch.cuda.synchronize()
+        g0, g1, r0, r1, f0, f1 = (_events(torch, reps) for _ in range(6))
+        for i in range(reps):
+            g0[i].record()
+            ll.kv_project(h, wk, wv, K, V)
+            g1[i].record()
+            r0[i].record()
+            cache.recache(0, K, V)
+            r1[i].record()
+            f0[i].record()
+            cache.recache_from_hidden(0, h, wk, wv)
+            f1[i].record()
+        torch.cuda.synchronize()
+        gms = sum(g0[i].elapsed_time(g1[i]) for i in range(reps)) / reps
+        rms = sum(r0[i].elapsed_time(r1[i]) for i in range(reps)) / reps
+        fms = sum(f0[i].elapsed_time(f1[i]) for i in range(reps)) / reps
+        flops = 2.0 * 2 * n * T * hid * hid
+        elt = 2 if kv == "bf16" else 1
+        # rewrite: read bf16 K/V, write slots (+ int8 scales)
+        wbytes = 2 * n * T * H * D * elt + (2 * n * T * H * 4 if kv == "int8" else 0)
+        rbytes = 2 * n * T * H * D * 2 + wbytes
+        cache.close()
+        if kv == "bf16":
+            res.update({"proj_ms": gms, "proj_tflops": flops / gms / 1e9,
+                        "proj_frac": flops / gms / 1e9 / PEAK_BF16_TFLOPS,
+                        "rewrite_us": rms * 1e3, "rewrite_bytes": rbytes, "rewrite_gbs": rbytes / rms / 1e6,
+                        "rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
+        else:
+            res.update({"int8_rewrite_us": rms * 1e3, "int8_rewrite_gbs": rbytes / rms / 1e6,
+                        "int8_rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
+        res[f"{kv}_unfused_ms"] = gms + rms
+        res[f"{kv}_fused_ms"] = fms
+        res[f"{kv}_fused_tflops"] = flops / fms / 1e9
+    return res
 
 
 def run_rollout(torch, ll, synth, cfg):
@@ -223,11 +244,14 @@ def run_window_sweep(torch, ll, synth, base, steps=10):
 
 
 def run_recache_stack(torch, ll, synth, cfg, reps=3):
-    """Recache of every layer: projection then rewrite per layer, then the next chunk's
-    attention on every layer (the prompt-switch workload)."""
+    """Recache of every layer at a prompt switch: per layer either projection then
+    rewrite, or the fused projection-into-slots (bf16 and int8 caches)."""
     r = run_recache_layer(torch, ll, synth, cfg, reps=reps)
-    stack_ms = cfg.layers * (r["proj_ms"] + r["rewrite_us"] / 1e3)
-    return {"workload": cfg.name, "layers": cfg.layers, "per_layer": r, "stack_ms_projection_plus_rewrite": stack_ms}
+    out = {"workload": cfg.name, "layers": cfg.layers, "per_layer": r}
+    for kv in ("bf16", "int8"):
+        out[f"stack_ms_{kv}_unfused"] = cfg.layers * r[f"{kv}_unfused_ms"]
+        out[f"stack_ms_{kv}_fused"] = cfg.layers * r[f"{kv}_fused_ms"]
+    return out
 
 
 def configs_mod():
@@ -343,6 +367,10 @@ def main():
             "recache_projection": {"ms": rc["proj_ms"], "tflops": rc["proj_tflops"], "frac_mfma": rc["proj_frac"]},
             "recache_rewrite": {"us": rc["rewrite_us"], "gbs": rc["rewrite_gbs"], "frac_hbm": rc["rewrite_frac"],
                                 "bytes": rc["rewrite_bytes"]},
+            "recache_int8_rewrite": {"us": rc["int8_rewrite_us"], "gbs": rc["int8_rewrite_gbs"],
+                                     "frac_hbm": rc["int8_rewrite_frac"]},
+            "recache_fused": {kv: {"ms": rc[f"{kv}_fused_ms"], "unfused_ms": rc[f"{kv}_unfused_ms"],
+                                   "tflops": rc[f"{kv}_fused_tflops"]} for kv in ("bf16", "int8")},
         }
 
     line = {

@@ -160,6 +160,24 @@ ll_status ll_cache_recache_window(ll_cache *c, int layer, const void *K_win,
 ll_status ll_kv_project(const void *h, const void *W_K, const void *W_V, int n_tokens,
                         int d_in, int d_out, void *K_all, void *V_all, void *stream);
 
+/*
+ * ll_cache_recache_from_hidden -- recache straight from hidden states: the
+ * projection of ll_kv_project with its results written into the retained slots
+ * (and, for int8 caches, quantised on the way) instead of into K_all/V_all.
+ * [LL-dpshk §三 items 4 and 5]: the retained latents' K and V are recomputed from
+ * the hidden state under the new prompt and replace the old cache.  The cache
+ * bytes equal those of ll_kv_project followed by ll_cache_recache bit for bit;
+ * the [n_frames*T][heads*head_dim] intermediate never reaches memory.
+ *   h         [n_frames*T][d_in] bf16, retained frames in logical order (sink
+ *             frames ascending, then window frames oldest to newest)
+ *   W_K, W_V  [heads*head_dim][d_in] bf16
+ *   n_frames  must equal min(f0, S+W) (else LL_ERR_STATE)
+ *   d_in      a multiple of 64; heads*head_dim must be a multiple of 128
+ * Errors: LL_ERR_INVALID, LL_ERR_STATE, LL_ERR_HIP.
+ */
+ll_status ll_cache_recache_from_hidden(ll_cache *c, int layer, const void *h, const void *W_K,
+                                       const void *W_V, int n_frames, int d_in, void *stream);
+
 /* ---- introspection (host-side, no device work) --------------------------- */
 
 /* Frames appended to `layer` so far (f0). */

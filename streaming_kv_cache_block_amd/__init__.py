@@ -26,7 +26,8 @@ MAX_SLOTS = 128
 
 EXPORTS = [
     "ll_cache_create", "ll_cache_destroy", "ll_cache_append", "ll_attn_sink_window",
-    "ll_cache_recache", "ll_cache_recache_window", "ll_kv_project", "ll_cache_frames_seen",
+    "ll_cache_recache", "ll_cache_recache_window", "ll_kv_project", "ll_cache_recache_from_hidden",
+    "ll_cache_frames_seen",
     "ll_cache_slot_frames", "ll_cache_slot_view", "ll_last_error",
 ]
 
@@ -58,6 +59,7 @@ def lib():
         "ll_cache_recache": [vp, i32, vp, vp, i32, vp],
         "ll_cache_recache_window": [vp, i32, vp, vp, i32, vp],
         "ll_kv_project": [vp, vp, vp, i32, i32, i32, vp, vp, vp],
+        "ll_cache_recache_from_hidden": [vp, i32, vp, vp, vp, i32, i32, vp],
         "ll_cache_frames_seen": [vp, i32, i64p],
         "ll_cache_slot_frames": [vp, i32, i64p],
         "ll_cache_slot_view": [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
@@ -155,6 +157,11 @@ class Cache:
     def recache_window(self, layer, K_win, V_win, n_frames=None, stream=None):
         _check(lib().ll_cache_recache_window(self._h, layer, _ptr(K_win), _ptr(V_win),
                                              self._frames(K_win, n_frames), _stream(stream)))
+
+    def recache_from_hidden(self, layer, h, W_K, W_V, n_frames=None, stream=None):
+        """Recache from hidden states h [n_frames*T][d_in]: K/V = h W^T written into the slots."""
+        _check(lib().ll_cache_recache_from_hidden(self._h, layer, _ptr(h), _ptr(W_K), _ptr(W_V),
+                                                  self._frames(h, n_frames), h.shape[1], _stream(stream)))
 
     def frames_seen(self, layer):
         v = ctypes.c_int64()

@@ -293,6 +293,47 @@ ll_status ll_kv_project(const void* h, const void* W_K, const void* W_V, int n_t
   return ok();
 }
 
+ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, const void* W_K, const void* W_V,
+                                       int n_frames, int d_in, void* stream) {
+  LL_TRY(check_layer(c, layer));
+  LL_TRY(check_tensor(h, "h"));
+  LL_TRY(check_tensor(W_K, "W_K"));
+  LL_TRY(check_tensor(W_V, "W_V"));
+  const int64_t d_out = int64_t(c->heads) * c->head_dim;
+  if (d_in < 64 || d_in % 64 != 0 || d_in > 65536) return fail(LL_ERR_INVALID, "d_in must be a multiple of 64");
+  if (d_out % 128 != 0 || d_out > 65536)
+    return fail(LL_ERR_INVALID, "heads*head_dim = %lld must be a multiple of 128", (long long)d_out);
+  const int64_t f0 = c->f0[size_t(layer)];
+  const int64_t need = ll::cached_frames(f0, c->S, c->W);
+  if (need == 0) return fail(LL_ERR_STATE, "recache_from_hidden: layer %d holds no frames", layer);
+  if (n_frames != need)
+    return fail(LL_ERR_STATE, "recache_from_hidden: n_frames must equal min(f0, S+W) = %lld (got %d)",
+                (long long)need, n_frames);
+  LL_TRY(check_frames(c, n_frames));
+  LL_TRY(check_device(c));
+  const std::vector<ll::WriteEntry> plan = ll::recache_plan(f0, c->S, c->W);
+  ll::ProjToCacheParams p{};
+  p.proj.h = static_cast<const uint16_t*>(h);
+  p.proj.WK = static_cast<const uint16_t*>(W_K);
+  p.proj.WV = static_cast<const uint16_t*>(W_V);
+  p.proj.M = n_frames * c->T;
+  p.proj.K = d_in;
+  p.proj.N = int(d_out);
+  p.T = c->T;
+  p.H = c->heads;
+  p.D = c->head_dim;
+  p.kv_int8 = c->kv_dtype == LL_KV_INT8;
+  p.slotK = c->k(layer);
+  p.slotV = c->v(layer);
+  p.scK = c->ks(layer);
+  p.scV = c->vs(layer);
+  p.n_plan = int(plan.size());
+  for (size_t i = 0; i < plan.size(); ++i) p.plan_slot[size_t(plan[i].src)] = plan[i].slot;
+  hipError_t e = ll::launch_kv_project_to_cache(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "recache_from_hidden launch");
+  return ok();
+}
+
 ll_status ll_cache_frames_seen(const ll_cache* c, int layer, int64_t* f0) {
   LL_TRY(check_layer(c, layer));
   if (!f0) return fail(LL_ERR_INVALID, "f0 is NULL");

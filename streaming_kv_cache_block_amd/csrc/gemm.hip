@@ -55,7 +55,118 @@ __device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t ld, int row
   }
 }
 
-__global__ __launch_bounds__(NT, 2) void proj_kernel(const ProjParams p, int n_mt, int n_units) {
+// Row of the cache slot array that output row m lands in: frame m / T goes to slot
+// plan_slot[m / T] (plan in LDS), token m % T.
+__device__ __forceinline__ int64_t slot_row(int m, int T, const int* plan) {
+  return int64_t(plan[m / T]) * T + m % T;
+}
+
+// Epilogue of the fused recache: bf16 results, or their int8 quantisation
+//   a = max |x| over the (token, head) row, scale = a / 127,
+//   q = clamp(rint((x * 127) / a), -127, 127)   (0 for an all-zero row),
+// with the quotient correctly rounded as in the int8 cache writer (one IEEE reciprocal
+// per row and a Markstein FMA correction; plain division where the absmax is below
+// 2^-100 or above 2^120).  x is the bf16-rounded sum, exactly what a separate
+// projection would have stored.
+template <int EPI>
+__device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, const f32x16 (&acc)[2][4], int m0, int n0,
+                                               int z, int wm, int wn, int g, int r32, int tid) {
+  __shared__ int plan[kMaxPlan];
+  __shared__ float amax[2][2][128];   // [wm][wn][token within the wave's half]
+  const ProjParams& p = pc.proj;
+  for (int i = tid; i < pc.n_plan; i += NT) plan[i] = pc.plan_slot[i];
+  __syncthreads();
+  const int N = p.N;
+  if constexpr (EPI == 1) {
+    uint16_t* base = static_cast<uint16_t*>(z ? pc.slotV : pc.slotK);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = m0 + 128 * wm + 32 * b + r32;
+      if (row >= p.M) continue;
+      uint16_t* dst = base + slot_row(row, pc.T, plan) * N + n0 + 64 * wn;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x2 w;
+          w.x = pack_bf16x2(acc[a][b][4 * i + 0], acc[a][b][4 * i + 1]);
+          w.y = pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3]);
+          *reinterpret_cast<u32x2*>(dst + 32 * a + 8 * i + 4 * g) = w;
+        }
+    }
+  } else {
+    // bf16-round, then the absmax of each (token, head) row: 32 values per lane, lanes
+    // g = 0/1 hold a wave's 64 outputs; with D = 128 the two output-half waves combine
+    // through LDS, with D = 64 a wave's 64 outputs are one head.
+    float x[4][2][16];
+    float am[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t bits = pack_bf16x2(acc[a][b][v], 0.0f) << 16;
+          x[b][a][v] = __builtin_bit_cast(float, bits);
+          mx = fmaxf(mx, fabsf(x[b][a][v]));
+        }
+      am[b] = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+    if (pc.D == 128) {
+      if (g == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) amax[wm][wn][32 * b + r32] = am[b];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < 4; ++b) am[b] = fmaxf(am[b], amax[wm][wn ^ 1][32 * b + r32]);
+    }
+    int8_t* base = static_cast<int8_t*>(z ? pc.slotV : pc.slotK);
+    float* sc = z ? pc.scV : pc.scK;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = m0 + 128 * wm + 32 * b + r32;
+      if (row >= p.M) continue;
+      const int64_t srow = slot_row(row, pc.T, plan);
+      const float a = am[b];
+      const bool plain = a < 0x1p-100f || a > 0x1p+120f;
+      const float y = 1.0f / a;
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t packed = 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            int qi = 0;
+            if (a > 0.0f) {
+              const float n = x[b][aa][4 * i + j] * 127.0f;
+              float qq;
+              if (plain) {
+                qq = n / a;
+              } else {
+                qq = n * y;
+                const float r = __builtin_fmaf(-a, qq, n);
+                qq = __builtin_fmaf(r, y, qq);
+              }
+              qi = int(fminf(fmaxf(__builtin_rintf(qq), -127.0f), 127.0f));
+            }
+            packed |= (uint32_t(qi) & 0xffu) << (8 * j);
+          }
+          const int n_out = n0 + 64 * wn + 32 * aa + 8 * i + 4 * g;
+          *reinterpret_cast<uint32_t*>(base + srow * N + n_out) = packed;
+        }
+      const int head = (n0 + 64 * wn) / pc.D;
+      if (g == 0 && (pc.D == 64 || wn == 0)) sc[srow * pc.H + head] = a / 127.0f;
+    }
+  }
+}
+
+// EPI 0: plain [M][N] outputs; 1: bf16 rows into cache slots; 2: int8 rows + scales.
+template <int EPI>
+__global__ __launch_bounds__(NT, 2) void proj_kernel(const ProjToCacheParams pc, int n_mt, int n_units) {
+  const ProjParams& p = pc.proj;
   __shared__ __attribute__((aligned(1024))) uint16_t sh0[TM * TK];
   __shared__ __attribute__((aligned(1024))) uint16_t sh1[TM * TK];
   __shared__ __attribute__((aligned(1024))) uint16_t sw0[TN * TK];
@@ -135,32 +246,51 @@ __global__ __launch_bounds__(NT, 2) void proj_kernel(const ProjParams p, int n_m
   if (st < nsteps) step(std::integral_constant<int, 0>{}, st, nsteps);
 
   // lane: token 128 wm + 32 b + r32, outputs 64 wn + 32 a + 8 i + 4 g + [0, 4)
+  if constexpr (EPI == 0) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int row = m0 + 128 * wm + 32 * b + r32;
-    if (row >= p.M) continue;
-    uint16_t* dst = out + int64_t(row) * p.N + n0 + 64 * wn;
+    for (int b = 0; b < 4; ++b) {
+      const int row = m0 + 128 * wm + 32 * b + r32;
+      if (row >= p.M) continue;
+      uint16_t* dst = out + int64_t(row) * p.N + n0 + 64 * wn;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w;
-        w.x = pack_bf16x2(acc[a][b][4 * i + 0], acc[a][b][4 * i + 1]);
-        w.y = pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3]);
-        *reinterpret_cast<u32x2*>(dst + 32 * a + 8 * i + 4 * g) = w;
-      }
+        for (int i = 0; i < 4; ++i) {
+          u32x2 w;
+          w.x = pack_bf16x2(acc[a][b][4 * i + 0], acc[a][b][4 * i + 1]);
+          w.y = pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3]);
+          *reinterpret_cast<u32x2*>(dst + 32 * a + 8 * i + 4 * g) = w;
+        }
+    }
+  } else {
+    cache_epilogue<EPI>(pc, acc, m0, n0, z, wm, wn, g, r32, tid);
   }
 }
 
 }  // namespace
 
-hipError_t launch_kv_project(const ProjParams& p, hipStream_t s) {
+namespace {
+template <int EPI>
+hipError_t launch_proj(const ProjToCacheParams& pc, hipStream_t s) {
+  const ProjParams& p = pc.proj;
   if (p.K % TK != 0 || p.N % TN != 0 || p.M <= 0) return hipErrorInvalidValue;
   const int n_mt = (p.M + TM - 1) / TM;
   const int n_units = n_mt * (p.N / TN) * 2;
   const int grid = (n_units + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL(proj_kernel, dim3(grid), dim3(NT), 0, s, p, n_mt, n_units);
+  hipLaunchKernelGGL((proj_kernel<EPI>), dim3(grid), dim3(NT), 0, s, pc, n_mt, n_units);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kv_project(const ProjParams& p, hipStream_t s) {
+  ProjToCacheParams pc{};
+  pc.proj = p;
+  return launch_proj<0>(pc, s);
+}
+
+hipError_t launch_kv_project_to_cache(const ProjToCacheParams& p, hipStream_t s) {
+  if (p.D != 64 && p.D != 128) return hipErrorInvalidValue;
+  return p.kv_int8 ? launch_proj<2>(p, s) : launch_proj<1>(p, s);
 }
 
 }  // namespace ll

@@ -58,4 +58,22 @@ struct ProjParams {
 
 hipError_t launch_kv_project(const ProjParams& p, hipStream_t s);
 
+// Projection whose epilogue writes straight into cache slots: output row m (frame
+// m / T, token m % T) goes to slot plan_slot[m / T]; N = H * D.  int8 caches get the
+// per-(token, head) quantisation of the bf16-rounded results (same bits as projecting,
+// then quantising the stored bf16 tensor).
+struct ProjToCacheParams {
+  ProjParams proj;      // outK/outV unused
+  int T, H, D;
+  bool kv_int8;
+  void* slotK;          // layer slot arrays [S+W][T][H][D]
+  void* slotV;
+  float* scK;           // int8: [S+W][T][H]
+  float* scV;
+  int n_plan;
+  int plan_slot[kMaxPlan];
+};
+
+hipError_t launch_kv_project_to_cache(const ProjToCacheParams& p, hipStream_t s);
+
 }  // namespace ll

@@ -71,6 +71,7 @@ def test_calls_on_null_handle_are_invalid(L):
     assert L.ll_attn_sink_window(None, 0, p16, p16, p16, 1, p16, None) == ll.LL_ERR_INVALID
     assert L.ll_cache_recache(None, 0, p16, p16, 1, None) == ll.LL_ERR_INVALID
     assert L.ll_cache_recache_window(None, 0, p16, p16, 1, None) == ll.LL_ERR_INVALID
+    assert L.ll_cache_recache_from_hidden(None, 0, p16, p16, p16, 1, 128, None) == ll.LL_ERR_INVALID
     f0 = ctypes.c_int64()
     assert L.ll_cache_frames_seen(None, 0, ctypes.byref(f0)) == ll.LL_ERR_INVALID
     L.ll_cache_destroy(None)
