@@ -45,6 +45,10 @@ namespace {
 constexpr int BN = 64;         // keys per tile
 constexpr int NXCD = 8;
 constexpr float kLazyThreshold = 8.0f;   // log2 units
+#ifndef LL_PIECE_TILES
+#define LL_PIECE_TILES 12
+#endif
+constexpr int kPieceTiles = LL_PIECE_TILES;   // per-piece overhead of a split walk, in tiles
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -111,6 +115,30 @@ __device__ __forceinline__ void dma_tile(const uint16_t* gk, const uint16_t* gv,
     __builtin_amdgcn_global_load_lds((gbl_void*)(gk + off), (lds_void*)(lk + r0 * D), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((gbl_void*)(gv + off), (lds_void*)(lv + r0 * D), 16, 0, 0);
   }
+}
+
+// Full bf16 tile: the per-lane byte offsets of the rows and chunks a wave copies are
+// the same for every tile (loff, computed once); the tile start only moves the
+// wave-uniform base pointers gk/gv.
+template <int D, int NW>
+__device__ __forceinline__ void dma_full(const uint16_t* gk, const uint16_t* gv, const uint32_t* loff,
+                                         uint16_t* lk, uint16_t* lv, int wave) {
+  using G = Geo<D, NW>;
+#pragma unroll
+  for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
+    const int r0 = (wave * G::DMA_PER_WAVE + i) * G::ROWS_PER_DMA;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(gk) + loff[i]),
+                                     (lds_void*)(lk + r0 * D), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(gv) + loff[i]),
+                                     (lds_void*)(lv + r0 * D), 16, 0, 0);
+  }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ uint32_t dma_lane_offset(int64_t rs, int wave, int lane, int i) {
+  using G = Geo<D, NW>;
+  const int r = (wave * G::DMA_PER_WAVE + i) * G::ROWS_PER_DMA + lane / G::CH;
+  return uint32_t((int64_t(r) * rs + 8 * swz<D>(r, lane % G::CH)) * 2);
 }
 
 // int8 cache tile: each wave copies whole rows of raw codes into a staging area
@@ -300,11 +328,9 @@ struct Attn {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float e = fast_exp2(__builtin_fmaf(S[qb][b][v], c, -mq));
-          rsum += e;
-          S[qb][b][v] = e;
+          S[qb][b][v] = fast_exp2(__builtin_fmaf(S[qb][b][v], c, -mq));
+          if (SCALED && scaled) rsum += S[qb][b][v];
         }
-      l[qb] += rsum;
       if (SCALED && scaled) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -315,6 +341,10 @@ struct Attn {
             for (int jj = 0; jj < 4; ++jj) S[qb][b][4 * i + jj] *= vscv[jj];
           }
       }
+      // Unscaled tiles: the row sum is taken over the bf16 probabilities that P*V uses
+      // (two per dot2), so the normalised weights sum to one exactly as applied.
+      // Scaled tiles sum the fp32 probabilities before the V scale (above).
+      const bool sum_packed = !(SCALED && scaled);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int b = u >> 1, v0 = 8 * (u & 1);
@@ -324,7 +354,14 @@ struct Attn {
         w.z = pack_bf16x2(S[qb][b][v0 + 4], S[qb][b][v0 + 5]);
         w.w = pack_bf16x2(S[qb][b][v0 + 6], S[qb][b][v0 + 7]);
         P[qb][u] = as_bf16x8(w);
+        if (sum_packed) {
+          rsum = dot2_ones(w.x, rsum);
+          rsum = dot2_ones(w.y, rsum);
+          rsum = dot2_ones(w.z, rsum);
+          rsum = dot2_ones(w.w, rsum);
+        }
       }
+      l[qb] += rsum;
     }
   }
 
@@ -386,6 +423,64 @@ struct Attn {
     }
   }
 
+  // Un-normalised O, reference max m and row sum l of this wave's rows, fp32, into a
+  // partial-result slot: O at [row][D], then m[rows], then l[rows] (row = the row
+  // within the block).  Device-coherent stores (they bypass the non-coherent caches),
+  // so another workgroup's device-coherent loads see them without a cache flush.
+  __device__ __forceinline__ void store_partial(float* slot, int rows, int wave) const {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = wave * 32 * NQB + 32 * qb + r32;
+      const float lt = l[qb] + __shfl_xor(l[qb], 32);
+      const __amdgpu_buffer_rsrc_t rsrc = coherent_rsrc(slot);
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          coherent_store4(rsrc, 4u * uint32_t(row * D + 32 * e + 8 * i + 4 * g),
+                          f32x4{O[qb][e][4 * i], O[qb][e][4 * i + 1], O[qb][e][4 * i + 2], O[qb][e][4 * i + 3]});
+      if (g == 0) {
+        coherent_store(slot + rows * D + row, m[qb]);
+        coherent_store(slot + rows * D + rows + row, lt);
+      }
+    }
+  }
+
+  // Combine this wave's own piece (registers) with the partial results of the other
+  // pieces of the block over disjoint key sets:
+  //   M = max_i m_i,  O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,
+  // then store.  The same identity as the running rescale inside one piece.
+  __device__ __forceinline__ void merge_store(const float* o0, const float* o1, int n_others, int rows, int wave,
+                                              uint16_t* out, int q0, int nq, int64_t rs, int h) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = wave * 32 * NQB + 32 * qb + r32;
+      float M = m[qb];
+      for (int k = 0; k < n_others; ++k) M = fmaxf(M, coherent_load((k ? o1 : o0) + rows * D + row));
+      const float fo = fast_exp2(m[qb] - M);
+      float L = (l[qb] + __shfl_xor(l[qb], 32)) * fo;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) O[qb][e] *= fo;
+      for (int k = 0; k < n_others; ++k) {
+        const float* sl = k ? o1 : o0;
+        const float f = fast_exp2(coherent_load(sl + rows * D + row) - M);
+        L += f * coherent_load(sl + rows * D + rows + row);
+        const __amdgpu_buffer_rsrc_t rsrc = coherent_rsrc(sl);
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 v = coherent_load4(rsrc, 4u * uint32_t(row * D + 32 * e + 8 * i + 4 * g));
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) O[qb][e][4 * i + jj] += f * v[jj];
+          }
+      }
+      // store() halves the row sum across the lane pair: hand it half of L per lane
+      l[qb] = 0.5f * L;
+    }
+    store(out, q0, nq, rs, h);
+  }
+
   // Q^T fragments (MFMA B operand): lane holds query r32, d = 16 s + 8 g + [0, 8).
   __device__ __forceinline__ void load_q(const uint16_t* Q, int q0, int nq, int64_t rs, int h, float c_) {
     c = c_;
@@ -406,8 +501,30 @@ struct Attn {
   }
 };
 
+// Per-XCD work plan of a split launch: blocks [b0, b0 + nb) run on this XCD, one
+// workgroup each for their first J - t tiles; ns spare workgroups take the tails, spare
+// s the tail units [s L, (s + 1) L) of the XCD (unit = one tile of one block's tail,
+// block-major).  L >= t, so a tail meets at most two spares and a block has at most
+// three pieces.
+struct XcdPlan {
+  int b0 = 0, nb = 0, ns = 0, t = 0, L = 0;
+  XcdPlan() = default;
+  __host__ __device__ XcdPlan(const Split& sp, int x) {
+    b0 = x * sp.B / NXCD;
+    nb = (x + 1) * sp.B / NXCD - b0;
+    ns = sp.per_xcd - nb;
+    // heads walk J - t tiles; a spare walks about nb t / ns tiles over about nb / ns + 1
+    // pieces, each costing ~kPieceTiles tiles of set-up and hand-over: equal times at
+    // t = J ns / (nb + ns) - kPieceTiles.
+    t = ns > 0 ? max(0, sp.J * ns / (nb + ns) - kPieceTiles) : 0;
+    L = t ? (nb * t + ns - 1) / ns : 0;
+  }
+  __host__ __device__ int first_spare(int b) const { return b * t / L; }
+  __host__ __device__ int n_tail(int b) const { return ((b + 1) * t - 1) / L - b * t / L + 1; }
+};
+
 template <int D, int NQB, int NW, int MINB, bool KV8>
-__global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p, int n_qtiles, int n_blocks) {
+__global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p, const Split sp) {
   using G = Geo<D, NW>;
   // Two buffers per operand as separate LDS objects: the buffer parity is a compile-time
   // constant at every access, which lets the compiler see that the copy into the next
@@ -421,101 +538,206 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   __shared__ __attribute__((aligned(16))) float sm_vs0[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(16))) float sm_vs1[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(1024))) int8_t sm_stage[KV8 ? 2 * Int8Tile<D, NW>::STAGE : 16];
-
-  // XCD-aware numbering: hardware deals block ids round-robin over the XCDs; give
-  // each XCD a contiguous range of logical blocks (query tiles of the same head).
-  const int per_xcd = (n_blocks + NXCD - 1) / NXCD;
-  const int bid = blockIdx.x;
-  const int logical = (bid % NXCD) * per_xcd + bid / NXCD;
-  if (logical >= n_blocks) return;
-  const int h = logical / n_qtiles;
-  const int qtile = logical % n_qtiles;
+  __shared__ int sm_last;
+  constexpr int ROWS = NW * 32 * NQB;   // query rows per block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t rs = int64_t(p.H) * D;
-  const int q0 = qtile * (NW * 32 * NQB) + wave * (32 * NQB);
 
   Attn<D, NQB, NW, KV8> A;
   A.init_offsets(lane);
-  A.load_q(p.Q, q0, p.nq, rs, h, p.c);
 
   const TileOrder order(p.ncache, p.nq);
   const int ntiles = order.total();
-  const uint16_t* ck = KV8 ? nullptr : static_cast<const uint16_t*>(p.cK) + int64_t(h) * D;
-  const uint16_t* cv = KV8 ? nullptr : static_cast<const uint16_t*>(p.cV) + int64_t(h) * D;
-  const uint16_t* kc = p.Kc + int64_t(h) * D;
-  const uint16_t* vc = p.Vc + int64_t(h) * D;
+  uint32_t loff[Geo<D, NW>::DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < Geo<D, NW>::DMA_PER_WAVE; ++i) loff[i] = dma_lane_offset<D, NW>(rs, wave, lane, i);
 
-  // Loads of tile j into buffer PB.  int8 tiles go to the staging area first and are
-  // widened by finish().  Returns true when a widening is pending.
-  auto issue = [&](auto pb, int j) __attribute__((always_inline)) -> bool {
-    constexpr int PB = decltype(pb)::value;
-    const TileInfo t = order.at(j);
-    if (KV8 && t.seg == 0) {
-      Int8Tile<D, NW>::issue(p, h, t, sm_stage, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, wave, lane);
-      return true;
+  // One piece: block blk (head, query tile) over key tiles [ja, jb) of the tile order,
+  // one of the block's npc pieces.  A whole block stores its output; otherwise the piece
+  // leaves a partial result in its slot and the last piece of the block to arrive
+  // merges them all.
+  auto piece = [&](int blk, int ja, int jb, int npc, int slot) __attribute__((always_inline)) {
+    const int h = blk / sp.n_qtiles;
+    const int q0 = (blk % sp.n_qtiles) * ROWS + wave * (32 * NQB);
+    const int jend = jb;
+    const uint16_t* ck = KV8 ? nullptr : static_cast<const uint16_t*>(p.cK) + int64_t(h) * D;
+    const uint16_t* cv = KV8 ? nullptr : static_cast<const uint16_t*>(p.cV) + int64_t(h) * D;
+    const uint16_t* kc = p.Kc + int64_t(h) * D;
+    const uint16_t* vc = p.Vc + int64_t(h) * D;
+    A.load_q(p.Q, q0, p.nq, rs, h, p.c);
+
+    // Loads of tile j into buffer PB.  int8 tiles go to the staging area first and are
+    // widened by finish().  Returns true when a widening is pending.
+    auto issue = [&](auto pb, int j) __attribute__((always_inline)) -> bool {
+      constexpr int PB = decltype(pb)::value;
+      const TileInfo t = order.at(j);
+      if (KV8 && t.seg == 0) {
+        Int8Tile<D, NW>::issue(p, h, t, sm_stage, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, wave, lane);
+        return true;
+      }
+      dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0,
+                      wave, lane);
+      return false;
+    };
+    // A full bf16 tile (every tile after the partial ones, except int8 cache tiles).
+    auto issue_full = [&](auto pb, int j) __attribute__((always_inline)) {
+      constexpr int PB = decltype(pb)::value;
+      const TileInfo t = order.at(j);
+      const int64_t base = int64_t(t.start) * rs;
+      dma_full<D, NW>((t.seg == 0 ? ck : kc) + base, (t.seg == 0 ? cv : vc) + base, loff, PB ? sm_k1 : sm_k0,
+                      PB ? sm_v1 : sm_v0, wave);
+    };
+    auto finish = [&](auto pb, bool pending) __attribute__((always_inline)) {
+      constexpr int PB = decltype(pb)::value;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (KV8 && pending) Int8Tile<D, NW>::widen(sm_stage, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, wave, lane);
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // Full tiles: prefetch the next tile into the other buffer, compute this one.  The
+    // buffer parity is a template argument so LDS accesses name a fixed buffer.
+    // KIND 1: int8 cache tiles (scaled), 2: bf16 tiles (cache or own chunk).
+    auto step = [&](auto pb, auto kind, int j) __attribute__((always_inline)) {
+      constexpr int PB = decltype(pb)::value;
+      constexpr int KIND = decltype(kind)::value;
+      bool pend = false;
+      if (j + 1 < jend) {
+        if (KIND == 2 || !KV8) {
+          issue_full(std::integral_constant<int, PB ^ 1>{}, j + 1);
+        } else {
+          pend = issue(std::integral_constant<int, PB ^ 1>{}, j + 1);
+        }
+      }
+      A.template tile<false, KIND == 1>(PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_ks1 : sm_ks0,
+                                        PB ? sm_vs1 : sm_vs0, BN);
+      finish(std::integral_constant<int, PB ^ 1>{}, pend);
+    };
+    auto run = [&](auto kind, int j, int end) __attribute__((always_inline)) -> int {
+      if (j < end && (j & 1)) step(I1{}, kind, j++);
+      for (; j + 1 < end; j += 2) {
+        step(I0{}, kind, j);
+        step(I1{}, kind, j + 1);
+      }
+      if (j < end) step(I0{}, kind, j++);
+      return j;
+    };
+
+    if (ja & 1) finish(I1{}, issue(I1{}, ja));
+    else finish(I0{}, issue(I0{}, ja));
+    int j = ja;
+    // Partial tiles (at most two): one generic masked path with run-time buffer choice.
+    for (; j < min(jb, order.npart()); ++j) {
+      bool pend = false;
+      if (j + 1 < jb) pend = (j & 1) ? issue(I0{}, j + 1) : issue(I1{}, j + 1);
+      const TileInfo t = order.at(j);
+      const bool odd = j & 1;
+      A.template tile<true, KV8>(odd ? sm_k1 : sm_k0, odd ? sm_v1 : sm_v0, odd ? sm_ks1 : sm_ks0,
+                                 odd ? sm_vs1 : sm_vs0, t.cnt, KV8 && t.seg == 0);
+      if (j & 1) finish(I0{}, pend);
+      else finish(I1{}, pend);
     }
-    dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0,
-                    wave, lane);
-    return false;
-  };
-  auto finish = [&](auto pb, bool pending) __attribute__((always_inline)) {
-    constexpr int PB = decltype(pb)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (KV8 && pending) Int8Tile<D, NW>::widen(sm_stage, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, wave, lane);
+    if (KV8) j = run(std::integral_constant<int, 1>{}, j, min(jb, order.full1_end()));
+    run(std::integral_constant<int, 2>{}, j, jb);
+
+    if (npc == 1) {
+      A.store(p.out, q0, p.nq, rs, h);
+      return;
+    }
+    // The partials go out with device-coherent stores; waiting for them to complete
+    // before the arrival count orders them before it for every observer.  The last
+    // piece reads the others with device-coherent loads after seeing the count.  No
+    // cache is flushed or invalidated (that would evict the key/value tiles the other
+    // workgroups of the XCD are streaming).
+    // A piece that finds every other piece already counted is the last one: it merges
+    // from its registers without leaving a partial (the common case for the head piece,
+    // which has the longest walk).
+    const int64_t slot_floats = split_slot_floats(D, ROWS);
+    if (tid == 0) sm_last = coherent_load(sp.cnt + blk) == npc - 1;
+    __syncthreads();
+    if (!sm_last) {
+      A.store_partial(sp.ws + slot * slot_floats, ROWS, wave);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) sm_last = atomicAdd(sp.cnt + blk, 1) == npc - 1;
+      __syncthreads();
+    }
+    if (sm_last) {
+      // the block's slots: blk (head piece), B + 2 blk + k (tail pieces k < npc - 1)
+      const int s0 = blk == slot ? sp.B + 2 * blk : blk;
+      const int s1 = sp.B + 2 * blk + ((blk == slot || sp.B + 2 * blk == slot) ? 1 : 0);
+      A.merge_store(sp.ws + s0 * slot_floats, sp.ws + s1 * slot_floats, npc - 1, ROWS, wave, p.out, q0, p.nq,
+                    rs, h);
+      if (tid == 0) coherent_store(sp.cnt + blk, 0);   // ready for the next call on the stream
+    }
     __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  // Full tiles: prefetch the next tile into the other buffer, compute this one.  The
-  // buffer parity is a template argument so LDS accesses name a fixed buffer.
-  // KIND 1: int8 cache tiles (scaled), 2: bf16 tiles (cache or own chunk).
-  auto step = [&](auto pb, auto kind, int j) __attribute__((always_inline)) {
-    constexpr int PB = decltype(pb)::value;
-    constexpr int KIND = decltype(kind)::value;
-    const bool pend = j + 1 < ntiles ? issue(std::integral_constant<int, PB ^ 1>{}, j + 1) : false;
-    A.template tile<false, KIND == 1>(PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_ks1 : sm_ks0,
-                                      PB ? sm_vs1 : sm_vs0, BN);
-    finish(std::integral_constant<int, PB ^ 1>{}, pend);
-  };
-  auto run = [&](auto kind, int j, int end) __attribute__((always_inline)) -> int {
-    if (j < end && (j & 1)) step(I1{}, kind, j++);
-    for (; j + 1 < end; j += 2) {
-      step(I0{}, kind, j);
-      step(I1{}, kind, j + 1);
+
+  // The pieces of this workgroup.  Plain launch: one workgroup per block (XCD-aware
+  // numbering: hardware deals block ids round-robin over the XCDs; each XCD gets a
+  // contiguous range of blocks, so query tiles of one head share its L2 while they
+  // stream the same keys).  Split launch: one workgroup per CU; on each XCD workgroup
+  // i < nb walks the first J - t tiles of its block (in step with the others, as
+  // above) and the ns = per_xcd - nb spare workgroups share the blocks' last t tiles
+  // ("tails"), so every CU gets about the same number of tiles.
+  const int J = ntiles;
+  if (!sp.on || int(blockIdx.x) / NXCD < XcdPlan(sp, blockIdx.x % NXCD).nb) {
+    int blk, jb = J, npc = 1;
+    if (!sp.on) {
+      const int per_xcd = (sp.B + NXCD - 1) / NXCD;
+      blk = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+      if (blk >= sp.B) return;
+    } else {
+      const XcdPlan xp(sp, blockIdx.x % NXCD);
+      const int i = blockIdx.x / NXCD;
+      blk = xp.b0 + i;
+      jb = J - xp.t;
+      npc = xp.t ? 1 + xp.n_tail(i) : 1;
     }
-    if (j < end) step(I0{}, kind, j++);
-    return j;
-  };
-
-  finish(I0{}, issue(I0{}, 0));
-  int j = 0;
-  // Partial tiles (at most two): one generic masked path with run-time buffer choice.
-  for (; j < order.npart(); ++j) {
-    bool pend = false;
-    if (j + 1 < ntiles) pend = (j & 1) ? issue(I0{}, j + 1) : issue(I1{}, j + 1);
-    const TileInfo t = order.at(j);
-    const bool odd = j & 1;
-    A.template tile<true, KV8>(odd ? sm_k1 : sm_k0, odd ? sm_v1 : sm_v0, odd ? sm_ks1 : sm_ks0,
-                               odd ? sm_vs1 : sm_vs0, t.cnt, KV8 && t.seg == 0);
-    if (j & 1) finish(I0{}, pend);
-    else finish(I1{}, pend);
+    piece(blk, 0, jb, npc, blk);
+    return;
   }
-  if (KV8) j = run(std::integral_constant<int, 1>{}, j, order.full1_end());
-  run(std::integral_constant<int, 2>{}, j, ntiles);
-
-  A.store(p.out, q0, p.nq, rs, h);
+  const XcdPlan xp(sp, blockIdx.x % NXCD);
+  const int sidx = int(blockIdx.x) / NXCD - xp.nb;
+  if (sidx >= xp.ns || xp.t == 0) return;
+  const int u1 = min((sidx + 1) * xp.L, xp.nb * xp.t);
+  for (int u = sidx * xp.L; u < u1;) {
+    const int bl = u / xp.t;
+    const int e = min(u1, (bl + 1) * xp.t);
+    const int blk = xp.b0 + bl;
+    const int ja = J - xp.t + (u - bl * xp.t);
+    piece(blk, ja, ja + (e - u), 1 + xp.n_tail(bl), sp.B + 2 * blk + (xp.first_spare(bl) == sidx ? 0 : 1));
+    u = e;
+  }
 }
+
 
 template <int D, int NQB, int NW, bool KV8, int MINB = 1>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const int rows = NW * 32 * NQB;
-  const int n_qtiles = (p.nq + rows - 1) / rows;
-  const int n_blocks = n_qtiles * p.H;
-  const int grid = (n_blocks + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KV8>), dim3(grid), dim3(64 * NW), 0, s, p, n_qtiles, n_blocks);
+  Split sp{};
+  sp.n_qtiles = (p.nq + rows - 1) / rows;
+  sp.B = sp.n_qtiles * p.H;
+  sp.J = (p.ncache + BN - 1) / BN + (p.nq + BN - 1) / BN;
+  sp.ws = p.ws;
+  sp.cnt = p.cnt;
+  // Split when the blocks leave CUs idle, every XCD has at least as many blocks as spare
+  // workgroups (so L >= t) and the walk is long enough to be worth a merge.
+  bool on = p.ws && p.cnt && p.n_cu % NXCD == 0 && sp.B < p.n_cu && sp.J >= 32 &&
+            split_slot_floats(D, rows) * 3 * int64_t(p.n_cu) <= p.ws_floats;
+  if (on) {
+    sp.per_xcd = p.n_cu / NXCD;
+    for (int x = 0; x < NXCD && on; ++x) {
+      const XcdPlan xp(sp, x);
+      on = xp.nb >= 1 && xp.nb >= xp.ns && (xp.t == 0 || xp.L >= xp.t);
+    }
+  }
+  sp.on = on;
+  const int grid = on ? p.n_cu : (sp.B + NXCD - 1) / NXCD * NXCD;
+  hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KV8>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
   return hipGetLastError();
 }
 

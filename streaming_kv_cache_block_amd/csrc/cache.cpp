@@ -31,6 +31,9 @@ struct ll_cache {
   int64_t rows_per_frame = 0;   // T * heads
   size_t kv_bytes = 0;          // one K (or V) slot array of one layer
   size_t sc_bytes = 0;          // one K (or V) scale array of one layer
+  int n_cu = 0;                 // compute units of the device
+  size_t ws_offset = 0;         // attention work-split buffers: partial results, then counters
+  int64_t ws_floats = 0;
   void* mem = nullptr;
   std::vector<int64_t> f0;
   std::vector<std::vector<int64_t>> slot_frame;
@@ -45,6 +48,8 @@ struct ll_cache {
     return sc_bytes ? reinterpret_cast<float*>(base() + size_t(2) * layers * kv_bytes + (size_t(2) * l + 1) * sc_bytes)
                     : nullptr;
   }
+  float* ws() const { return reinterpret_cast<float*>(base() + ws_offset); }
+  int* cnt() const { return reinterpret_cast<int*>(base() + ws_offset + size_t(ws_floats) * 4); }
 };
 
 namespace {
@@ -154,17 +159,31 @@ ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_fr
   auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
   const int64_t kv_bytes = round256(slots * rows * head_dim * elt);
   const int64_t sc_bytes = kv_dtype == LL_KV_INT8 ? round256(slots * rows * 4) : 0;
-  const double total = double(layers) * 2.0 * double(kv_bytes + sc_bytes);
-  if (total > double(int64_t(1) << 46)) return fail(LL_ERR_INVALID, "cache too large (%.3g bytes)", total);
+  const double cache_total = double(layers) * 2.0 * double(kv_bytes + sc_bytes);
+  if (cache_total > double(int64_t(1) << 46)) return fail(LL_ERR_INVALID, "cache too large (%.3g bytes)", cache_total);
 
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int n_cu = 0;
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  // Work-split buffers of the attention launch (partial results of at most three pieces
+  // per block, blocks < CUs; one arrival counter per CU), after the cache arrays.
+  const int64_t ws_floats = ll::split_ws_floats(head_dim, n_cu);
+  const int64_t ws_offset = int64_t(cache_total);
+  const double total = cache_total + double(ws_floats) * 4 + double(round256(int64_t(n_cu) * 4));
   void* mem = nullptr;
   e = hipMalloc(&mem, size_t(total));
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(LL_ERR_OOM, "hipMalloc of %.3g bytes failed: %s", total, hipGetErrorString(e));
+  }
+  e = hipMemset(static_cast<char*>(mem) + ws_offset + ws_floats * 4, 0, size_t(n_cu) * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    return hip_fail(e, "clearing the work-split counters");
   }
   ll_cache* c = new ll_cache;
   c->layers = layers;
@@ -178,6 +197,9 @@ ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_fr
   c->rows_per_frame = rows;
   c->kv_bytes = size_t(kv_bytes);
   c->sc_bytes = size_t(sc_bytes);
+  c->n_cu = n_cu;
+  c->ws_offset = size_t(ws_offset);
+  c->ws_floats = ws_floats;
   c->mem = mem;
   c->f0.assign(size_t(layers), 0);
   c->slot_frame.assign(size_t(layers), std::vector<int64_t>(size_t(slots), -1));
@@ -228,6 +250,10 @@ ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void*
   p.ncache = int(n_vis * c->T);
   p.H = c->heads;
   p.c = float(1.4426950408889634 / std::sqrt(double(c->head_dim)));
+  p.ws = c->ws();
+  p.ws_floats = c->ws_floats;
+  p.cnt = c->cnt();
+  p.n_cu = c->n_cu;
   hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype == LL_KV_INT8, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();

@@ -32,6 +32,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Device-scope (all XCDs) coherent load/store of one word: relaxed atomics at agent
+// scope, which go past the per-XCD caches instead of relying on a cache flush.
+template <typename T>
+__device__ __forceinline__ void coherent_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T coherent_load(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The same for 16 bytes, through a buffer resource over [base, base + 2 GiB) with the
+// agent-scope cache policy (sc1); byte offsets are 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16);
+}
+__device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
+}
+
+// acc + lo + hi of a packed bf16 pair (one v_dot2 against (1, 1)).
+__device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 // Select 16-bit halves: result = (b.half[hb] << 16) | a.half[ha].
 __device__ __forceinline__ uint32_t pick_lo_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

@@ -23,7 +23,32 @@ struct AttnParams {
   int ncache;           // cached key rows
   int H;
   float c;              // log2(e) / sqrt(D)
+  // Work-split buffers (owned by the cache; may be null: then no split): partial
+  // results and per-block arrival counters (all zero between calls), CU count.
+  float* ws;
+  int64_t ws_floats;
+  int* cnt;
+  int n_cu;
 };
+
+// Floats of one partial-result slot: O [rows][D] + m [rows] + l [rows], 256-byte aligned.
+inline __host__ __device__ int64_t split_slot_floats(int D, int rows) {
+  return (int64_t(rows) * (D + 2) + 63) / 64 * 64;
+}
+
+// Work description of one attention launch (device side: attn.hip).
+struct Split {
+  int B;          // blocks = heads x query tiles
+  int n_qtiles;
+  int J;          // key tiles per block
+  int on;         // 1: one workgroup per CU, tails of the key walk shared (per XCD)
+  int per_xcd;    // workgroups per XCD when on
+  float* ws;
+  int* cnt;
+};
+
+// Partial-result slots a split launch may use: blocks < CUs, three pieces at most.
+inline int64_t split_ws_floats(int D, int n_cu) { return split_slot_floats(D, 256) * 3 * int64_t(n_cu); }
 
 hipError_t launch_attention(const AttnParams& p, int D, bool kv_int8, hipStream_t s);
 
