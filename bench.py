@@ -9,8 +9,9 @@ tensors generated on the device before the timed region (a pool of fresh Q/K/V
 sets, one per pass, reused cyclically across steps).
 
 Prints ONE JSON line with the whole-step throughput in latent frames/s per layer,
-the attention kernel's roofline position, component timings (int8 cache, recache
-projection and rewrite) and the CPU oracle timed on this host as a baseline.
+the attention kernel's roofline position, component timings (int8 and fp8 caches,
+recache projection, rewrite and the fused projection-into-slots) and the CPU oracle
+timed on this host as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -61,11 +62,12 @@ def _attn_flops(H, D, nq, nk):
     return 4.0 * H * D * nq * nk
 
 
-def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False):
+def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
     """The timed step loop; returns a dict of measurements."""
+    kv = kv or ("int8" if kv_int8 else "bf16")
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     shape = (cfg.nq, H, D)
-    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8" if kv_int8 else "bf16")
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     prefill = (S + W + C - 1) // C + 1
     for k in range(prefill):
         cache.append(0, synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, 1, 0, k),
@@ -105,9 +107,9 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False):
     wall = time.perf_counter() - t0
     attn_ms = [a0[j].elapsed_time(a1[j]) for j in range(steps * P)]
     app_ms = [b0[i].elapsed_time(b1[i]) for i in range(steps)]
-    elt = 1 if kv_int8 else 2
+    elt = 1 if kv != "bf16" else 2
     rows = C * T * H
-    app_bytes = 2 * rows * D * 2 + 2 * rows * D * elt + (2 * rows * 4 if kv_int8 else 0)
+    app_bytes = 2 * rows * D * 2 + 2 * rows * D * elt + (2 * rows * 4 if kv != "bf16" else 0)
     attn_avg = sum(attn_ms) / len(attn_ms)
     app_avg = sum(app_ms) / len(app_ms)
     flops = _attn_flops(H, D, cfg.nq, nk)
@@ -129,7 +131,7 @@ def run_recache_layer(torch, ll, synth, cfg, reps=10):
     hid = cfg.hidden
     shape = (cfg.nq, H, D)
     res = {}
-    for kv in ("bf16", "int8"):
+    for kv in ("bf16", "int8", "fp8"):
         cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
         for k in range(cfg.prefill_chunks):
             cache.append(0, synth.normal_bf16_device(shape, 1.0, cfg.seed, 1, k),
@@ -169,8 +171,8 @@ def run_recache_layer(torch, ll, synth, cfg, reps=10):
                         "rewrite_us": rms * 1e3, "rewrite_bytes": rbytes, "rewrite_gbs": rbytes / rms / 1e6,
                         "rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
         else:
-            res.update({"int8_rewrite_us": rms * 1e3, "int8_rewrite_gbs": rbytes / rms / 1e6,
-                        "int8_rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
+            res.update({f"{kv}_rewrite_us": rms * 1e3, f"{kv}_rewrite_gbs": rbytes / rms / 1e6,
+                        f"{kv}_rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
         res[f"{kv}_unfused_ms"] = gms + rms
         res[f"{kv}_fused_ms"] = fms
         res[f"{kv}_fused_tflops"] = flops / fms / 1e9
@@ -248,7 +250,7 @@ def run_recache_stack(torch, ll, synth, cfg, reps=3):
     rewrite, or the fused projection-into-slots (bf16 and int8 caches)."""
     r = run_recache_layer(torch, ll, synth, cfg, reps=reps)
     out = {"workload": cfg.name, "layers": cfg.layers, "per_layer": r}
-    for kv in ("bf16", "int8"):
+    for kv in ("bf16", "int8", "fp8"):
         out[f"stack_ms_{kv}_unfused"] = cfg.layers * r[f"{kv}_unfused_ms"]
         out[f"stack_ms_{kv}_fused"] = cfg.layers * r[f"{kv}_fused_ms"]
     return out
@@ -353,7 +355,8 @@ def main():
     if not args.no_components:
         i8 = configs.Workload(**{**cfg.__dict__, "window": configs.LONG_INT8.window, "kv_int8": True,
                                  "seed": configs.LONG_INT8.seed})
-        r8 = run_steady(torch, ll, synth, i8, max(5, args.steps // 5), 2, kv_int8=True)
+        r8 = run_steady(torch, ll, synth, i8, max(5, args.steps // 5), 2, kv="int8")
+        rf8 = run_steady(torch, ll, synth, i8, max(5, args.steps // 5), 2, kv="fp8")
         rc = run_recache_layer(torch, ll, synth, configs.RECACHE)
         components = {
             "attention_bf16": {"ms": r["attn_ms"], "tflops": r["attn_tflops"],
@@ -364,13 +367,19 @@ def main():
                                    "frac_mfma": r8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r8["keys"]},
             "append_int8_w21": {"us": r8["append_us"], "gbs": r8["append_gbs"],
                                 "frac_hbm": r8["append_gbs"] / PEAK_HBM_GBS, "bytes": r8["append_bytes"]},
+            "attention_fp8_w21": {"ms": rf8["attn_ms"], "tflops": rf8["attn_tflops"],
+                                  "frac_mfma": rf8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": rf8["keys"]},
+            "append_fp8_w21": {"us": rf8["append_us"], "gbs": rf8["append_gbs"],
+                               "frac_hbm": rf8["append_gbs"] / PEAK_HBM_GBS, "bytes": rf8["append_bytes"]},
             "recache_projection": {"ms": rc["proj_ms"], "tflops": rc["proj_tflops"], "frac_mfma": rc["proj_frac"]},
             "recache_rewrite": {"us": rc["rewrite_us"], "gbs": rc["rewrite_gbs"], "frac_hbm": rc["rewrite_frac"],
                                 "bytes": rc["rewrite_bytes"]},
             "recache_int8_rewrite": {"us": rc["int8_rewrite_us"], "gbs": rc["int8_rewrite_gbs"],
                                      "frac_hbm": rc["int8_rewrite_frac"]},
+            "recache_fp8_rewrite": {"us": rc["fp8_rewrite_us"], "gbs": rc["fp8_rewrite_gbs"],
+                                    "frac_hbm": rc["fp8_rewrite_frac"]},
             "recache_fused": {kv: {"ms": rc[f"{kv}_fused_ms"], "unfused_ms": rc[f"{kv}_unfused_ms"],
-                                   "tflops": rc[f"{kv}_fused_tflops"]} for kv in ("bf16", "int8")},
+                                   "tflops": rc[f"{kv}_fused_tflops"]} for kv in ("bf16", "int8", "fp8")},
         }
 
     line = {

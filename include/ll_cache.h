@@ -42,7 +42,7 @@ extern "C" {
 
 typedef struct ll_cache ll_cache; /* opaque; owns its slot memory */
 
-typedef enum { LL_KV_BF16 = 0, LL_KV_INT8 = 1 } ll_kv_dtype;
+typedef enum { LL_KV_BF16 = 0, LL_KV_INT8 = 1, LL_KV_FP8 = 2 } ll_kv_dtype;
 
 typedef enum {
   LL_OK = 0,
@@ -71,12 +71,22 @@ typedef enum {
  *                     LL_KV_INT8: cached K/V stored as int8 codes with one fp32 scale
  *                     per (token, head) row:  scale = absmax/127,
  *                     q = clamp(rint((x*127)/absmax), -127, 127), 0 for an all-zero row
+ *                     LL_KV_FP8: OCP E4M3 codes (sign, 4 exponent bits with bias 7,
+ *                     3 mantissa bits; largest finite value 448) with one fp32 scale
+ *                     per row: scale = absmax/448, q = E4M3(clamp((x*448)/absmax,
+ *                     -448, 448)) rounded to nearest, ties to even, all-zero codes for
+ *                     an all-zero row (the clamp acts only where x*448 overflows).
+ *                     [LL2-wmrh §15.2-§15.3]: the history cache kept in low precision
+ *                     and dequantised where it is used.
+ *                     Every division above is one IEEE binary32 division.
  *   out               receives the handle
  *
  * Device memory: layers * 2 * (S+W) * T * heads * head_dim * (2 or 1) bytes, plus
- * layers * 2 * (S+W) * T * heads * 4 bytes of scales for int8.  Slot contents start
- * undefined; no slot is visible until written.  Errors: LL_ERR_INVALID, LL_ERR_OOM,
- * LL_ERR_HIP.
+ * layers * 2 * (S+W) * T * heads * 4 bytes of scales for int8 / fp8, plus a fixed
+ * attention work area (partial results of split key walks: 3 * CUs * 256 rows *
+ * (head_dim + 2) * 4 bytes, about 100 MB for head_dim 128 on 256 CUs).  Slot contents
+ * start undefined; no slot is visible until written.  Errors: LL_ERR_INVALID,
+ * LL_ERR_OOM, LL_ERR_HIP.
  */
 ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_frame,
                           int sink_frames, int window_frames, int kv_dtype,
@@ -109,8 +119,8 @@ ll_status ll_cache_append(ll_cache *c, int layer, const void *K, const void *V,
  * with full visibility inside the own chunk:
  *     out = softmax((Q K^T) / sqrt(head_dim)) V   per head, over those keys.
  * The cache is read only (denoise passes of one chunk may call this repeatedly).
- * For LL_KV_INT8 caches the cached keys/values are dequantised (q * scale); the own
- * chunk is used as given.
+ * For LL_KV_INT8 / LL_KV_FP8 caches the cached keys/values are dequantised
+ * (value(q) * scale); the own chunk is used as given.
  *   Q, K_chunk, V_chunk   [n_frames*T][heads][head_dim] bf16 (n_frames >= 1)
  *   out                   [n_frames*T][heads][head_dim] bf16, written completely
  * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax statistics, bf16
@@ -188,8 +198,8 @@ ll_status ll_cache_frames_seen(const ll_cache *c, int layer, int64_t *f0);
 ll_status ll_cache_slot_frames(const ll_cache *c, int layer, int64_t *frame_of_slot);
 
 /* Device pointers of `layer`'s slot arrays (read them after synchronising):
- *   K, V        [S+W][T][heads][head_dim], bf16 or int8 (kv_dtype)
- *   K_scale, V_scale  [S+W][T][heads] fp32 for int8 caches, NULL for bf16
+ *   K, V        [S+W][T][heads][head_dim], bf16, int8 or E4M3 bytes (kv_dtype)
+ *   K_scale, V_scale  [S+W][T][heads] fp32 for int8 / fp8 caches, NULL for bf16
  * Any output pointer may be NULL. */
 ll_status ll_cache_slot_view(const ll_cache *c, int layer, void **K, void **V,
                              void **K_scale, void **V_scale);

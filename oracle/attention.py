@@ -98,16 +98,17 @@ def _widen(bits, dtype):
 
 
 def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
-                    kv_int8=False, rows=None, dtype=np.float32):
+                    kv_int8=False, rows=None, dtype=np.float32, kv=None):
     """Attention of one chunk over V(f0), straight from the definition.
 
     Q, K_chunk, V_chunk: uint16 bf16 bits, shape [C*T][H][D] (own chunk).
     history(f) -> (K_f, V_f): uint16 bf16 bits [T][H][D], the K/V that frame
         f had when it entered the cache (or the recache tensor that replaced
         it).  Only frames in V(f0) are requested.
-    kv_int8: cached frames pass through the int8 per-(token, head) absmax
-        rule and are dequantised before use (own-chunk K/V are never
-        quantised).
+    kv: cache format "bf16" (default), "int8" or "fp8": for the last two the
+        cached frames pass through the per-(token, head) absmax rule of that
+        format (oracle.quant) and are dequantised before use; own-chunk K/V
+        are never quantised.  kv_int8=True is the same as kv="int8".
     rows: optional list of query rows to compute (sampled checks).
     Returns O [len(rows) or C*T][H][D] in ``dtype``.
 
@@ -116,6 +117,10 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
     only frames it marks visible contribute keys (a masked key has weight 0
     by definition, so leaving it out is the same computation).
     """
+    if kv is None:
+        kv = "int8" if kv_int8 else "bf16"
+    if kv not in ("bf16", "int8", "fp8"):
+        raise ValueError(f"unknown cache format {kv!r}")
     T = tokens_per_frame
     nq_all, H, D = Q.shape
     if nq_all % T:
@@ -132,9 +137,12 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
             Vs.append(_widen(V_chunk[a:a + T], dtype))
         else:
             kf, vf = history(f)
-            if kv_int8:
+            if kv == "int8":
                 Ks.append(_quant.dequantize(*_quant.quantize(_bf16.to_f32(kf))).astype(dtype))
                 Vs.append(_quant.dequantize(*_quant.quantize(_bf16.to_f32(vf))).astype(dtype))
+            elif kv == "fp8":
+                Ks.append(_quant.dequantize_fp8(*_quant.quantize_fp8(_bf16.to_f32(kf))).astype(dtype))
+                Vs.append(_quant.dequantize_fp8(*_quant.quantize_fp8(_bf16.to_f32(vf))).astype(dtype))
             else:
                 Ks.append(_widen(kf, dtype))
                 Vs.append(_widen(vf, dtype))

@@ -21,7 +21,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllcache.so")
 
 LL_OK, LL_ERR_INVALID, LL_ERR_OOM, LL_ERR_STATE, LL_ERR_HIP = range(5)
-LL_KV_BF16, LL_KV_INT8 = 0, 1
+LL_KV_BF16, LL_KV_INT8, LL_KV_FP8 = 0, 1, 2
+_KV_NAMES = {"bf16": LL_KV_BF16, "int8": LL_KV_INT8, "fp8": LL_KV_FP8}
 MAX_SLOTS = 128
 
 EXPORTS = [
@@ -111,9 +112,10 @@ class Cache:
         self.layers, self.heads, self.head_dim = layers, heads, head_dim
         self.T, self.S, self.W = tokens_per_frame, sink, window
         self.kv_dtype = kv_dtype
-        if kv_dtype not in ("bf16", "int8", LL_KV_BF16, LL_KV_INT8):
-            raise ValueError(f"kv_dtype must be 'bf16' or 'int8', got {kv_dtype!r}")
-        dt = {"bf16": LL_KV_BF16, "int8": LL_KV_INT8}.get(kv_dtype, kv_dtype)
+        if kv_dtype not in _KV_NAMES and kv_dtype not in _KV_NAMES.values():
+            raise ValueError(f"kv_dtype must be 'bf16', 'int8' or 'fp8', got {kv_dtype!r}")
+        dt = _KV_NAMES.get(kv_dtype, kv_dtype)
+        self.kv_code = dt
         h = ctypes.c_void_p()
         _check(lib().ll_cache_create(layers, heads, head_dim, tokens_per_frame, sink, window, dt,
                                      ctypes.byref(h)))
@@ -183,14 +185,14 @@ class Cache:
         """Copy the layer's slot arrays to the host (synchronising the device first).
 
         Returns a dict with 'K', 'V' as uint8 byte arrays shaped [S+W][T][H][D*elt]
-        and, for int8 caches, 'K_scale', 'V_scale' as float32 [S+W][T][H].
+        and, for int8 / fp8 caches, 'K_scale', 'V_scale' as float32 [S+W][T][H].
         """
         import numpy as np
         import torch
         torch.cuda.synchronize()
         kp, vp, ksp, vsp = self.slot_view(layer)
         slots = self.S + self.W
-        elt = 1 if self.kv_dtype in ("int8", LL_KV_INT8) else 2
+        elt = 1 if self.kv_code != LL_KV_BF16 else 2
         nbytes = slots * self.T * self.heads * self.head_dim * elt
         out = {"K": _d2h(kp, nbytes).reshape(slots, self.T, self.heads, self.head_dim * elt),
                "V": _d2h(vp, nbytes).reshape(slots, self.T, self.heads, self.head_dim * elt)}

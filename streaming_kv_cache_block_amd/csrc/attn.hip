@@ -141,13 +141,14 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int64_t rs, int wave, int la
   return uint32_t((int64_t(r) * rs + 8 * swz<D>(r, lane % G::CH)) * 2);
 }
 
-// int8 cache tile: each wave copies whole rows of raw codes into a staging area
-// (load-to-LDS, natural [row][D bytes] layout) and, after its own copies have landed,
-// widens exactly those rows to bf16 in the swizzled tile buffer (exact for |q| <= 127).
+// Quantised cache tile (int8 or fp8 codes): each wave copies whole rows of raw codes
+// into a staging area (load-to-LDS, natural [row][D bytes] layout) and, after its own
+// copies have landed, widens exactly those rows to bf16 in the swizzled tile buffer
+// (exact: |q| <= 127, and every E4M3 value is a bf16 value).
 // No wave reads another wave's staging rows, so no barrier is needed in between.  The
 // per-row scales are copied straight into their LDS arrays by waves 0 (K) and 1 (V).
-template <int D, int NW>
-struct Int8Tile {
+template <int D, int NW, int FMT>
+struct QTile {
   static constexpr int CH8 = D / 16;                 // 16-byte chunks per int8 row
   static constexpr int ROWS = 64 / CH8;              // rows per wave-wide 1 KB copy
   static constexpr int COPIES = BN / ROWS;           // copies per operand per tile
@@ -183,9 +184,11 @@ struct Int8Tile {
         const u32x4 q = *reinterpret_cast<const u32x4*>(stage + op * STAGE + i * ROWS * D + 16 * lane);
         uint16_t* dst = op ? lv : lk;
         *reinterpret_cast<u32x4*>(dst + r * D + 8 * swz<D>(r, 2 * c16)) =
-            u32x4{i8x2_to_bf16x2(q.x, 0), i8x2_to_bf16x2(q.x, 2), i8x2_to_bf16x2(q.y, 0), i8x2_to_bf16x2(q.y, 2)};
+            u32x4{code2_to_bf16x2<FMT>(q.x, 0), code2_to_bf16x2<FMT>(q.x, 2), code2_to_bf16x2<FMT>(q.y, 0),
+                  code2_to_bf16x2<FMT>(q.y, 2)};
         *reinterpret_cast<u32x4*>(dst + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
-            u32x4{i8x2_to_bf16x2(q.z, 0), i8x2_to_bf16x2(q.z, 2), i8x2_to_bf16x2(q.w, 0), i8x2_to_bf16x2(q.w, 2)};
+            u32x4{code2_to_bf16x2<FMT>(q.z, 0), code2_to_bf16x2<FMT>(q.z, 2), code2_to_bf16x2<FMT>(q.w, 0),
+                  code2_to_bf16x2<FMT>(q.w, 2)};
       }
     }
   }
@@ -523,7 +526,7 @@ struct XcdPlan {
   __host__ __device__ int n_tail(int b) const { return ((b + 1) * t - 1) / L - b * t / L + 1; }
 };
 
-template <int D, int NQB, int NW, int MINB, bool KV8>
+template <int D, int NQB, int NW, int MINB, int KVQ>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p, const Split sp) {
   using G = Geo<D, NW>;
   // Two buffers per operand as separate LDS objects: the buffer parity is a compile-time
@@ -533,11 +536,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   __shared__ __attribute__((aligned(1024))) uint16_t sm_k1[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v0[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v1[G::TILE];
+  constexpr bool KV8 = KVQ != kKvBf16;   // quantised cache (int8 or fp8 codes)
   __shared__ __attribute__((aligned(16))) float sm_ks0[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(16))) float sm_ks1[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(16))) float sm_vs0[KV8 ? BN : 1];
   __shared__ __attribute__((aligned(16))) float sm_vs1[KV8 ? BN : 1];
-  __shared__ __attribute__((aligned(1024))) int8_t sm_stage[KV8 ? 2 * Int8Tile<D, NW>::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t sm_stage[KV8 ? 2 * QTile<D, NW, KVQ>::STAGE : 16];
   __shared__ int sm_last;
   constexpr int ROWS = NW * 32 * NQB;   // query rows per block
 
@@ -575,7 +579,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
       constexpr int PB = decltype(pb)::value;
       const TileInfo t = order.at(j);
       if (KV8 && t.seg == 0) {
-        Int8Tile<D, NW>::issue(p, h, t, sm_stage, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, wave, lane);
+        QTile<D, NW, KVQ>::issue(p, h, t, sm_stage, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, wave, lane);
         return true;
       }
       dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0,
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
     auto finish = [&](auto pb, bool pending) __attribute__((always_inline)) {
       constexpr int PB = decltype(pb)::value;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (KV8 && pending) Int8Tile<D, NW>::widen(sm_stage, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, wave, lane);
+      if (KV8 && pending) QTile<D, NW, KVQ>::widen(sm_stage, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, wave, lane);
       __syncthreads();
     };
     using I0 = std::integral_constant<int, 0>;
@@ -715,7 +719,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
 }
 
 
-template <int D, int NQB, int NW, bool KV8, int MINB = 1>
+template <int D, int NQB, int NW, int KVQ, int MINB = 1>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const int rows = NW * 32 * NQB;
   Split sp{};
@@ -737,29 +741,28 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   }
   sp.on = on;
   const int grid = on ? p.n_cu : (sp.B + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KV8>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
+  hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KVQ>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p, int D, bool kv_int8, hipStream_t s) {
+hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t s) {
 // 8 waves of 32 query rows: two waves per SIMD, so one wave's softmax overlaps the
 // other's MFMAs and every accumulator fits the 256 architected VGPRs.
-#ifndef LL_ATTN_NQB
-#define LL_ATTN_NQB 1
-#define LL_ATTN_NW 8
-#define LL_ATTN_MINB 1
-#endif
   const bool big = p.nq > 4 * 32;
   if (D == 128) {
-    if (kv_int8)
-      return big ? launch_t<128, LL_ATTN_NQB, LL_ATTN_NW, true, LL_ATTN_MINB>(p, s) : launch_t<128, 1, 4, true>(p, s);
-    return big ? launch_t<128, LL_ATTN_NQB, LL_ATTN_NW, false, LL_ATTN_MINB>(p, s) : launch_t<128, 1, 4, false>(p, s);
-  }
-  if (D == 64) {
-    if (kv_int8) return big ? launch_t<64, 2, 4, true>(p, s) : launch_t<64, 1, 4, true>(p, s);
-    return big ? launch_t<64, 2, 4, false>(p, s) : launch_t<64, 1, 4, false>(p, s);
+    switch (kv_fmt) {
+      case kKvBf16: return big ? launch_t<128, 1, 8, kKvBf16>(p, s) : launch_t<128, 1, 4, kKvBf16>(p, s);
+      case kKvInt8: return big ? launch_t<128, 1, 8, kKvInt8>(p, s) : launch_t<128, 1, 4, kKvInt8>(p, s);
+      case kKvFp8: return big ? launch_t<128, 1, 8, kKvFp8>(p, s) : launch_t<128, 1, 4, kKvFp8>(p, s);
+    }
+  } else if (D == 64) {
+    switch (kv_fmt) {
+      case kKvBf16: return big ? launch_t<64, 2, 4, kKvBf16>(p, s) : launch_t<64, 1, 4, kKvBf16>(p, s);
+      case kKvInt8: return big ? launch_t<64, 2, 4, kKvInt8>(p, s) : launch_t<64, 1, 4, kKvInt8>(p, s);
+      case kKvFp8: return big ? launch_t<64, 2, 4, kKvFp8>(p, s) : launch_t<64, 1, 4, kKvFp8>(p, s);
+    }
   }
   return hipErrorInvalidValue;
 }

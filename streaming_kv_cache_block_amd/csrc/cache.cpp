@@ -129,7 +129,7 @@ ll_status write_frames(ll_cache* c, int layer, const void* K, const void* V, con
     wp.plan_src[i] = plan[i].src;
     wp.plan_slot[i] = plan[i].slot;
   }
-  hipError_t e = ll::launch_kv_write(wp, c->head_dim, c->kv_dtype == LL_KV_INT8, s);
+  hipError_t e = ll::launch_kv_write(wp, c->head_dim, c->kv_dtype, s);
   if (e != hipSuccess) return hip_fail(e, what);
   return LL_OK;
 }
@@ -152,13 +152,15 @@ ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_fr
   const int64_t slots = int64_t(sink_frames) + window_frames;
   if (slots < 1 || slots > LL_MAX_SLOTS)
     return fail(LL_ERR_INVALID, "sink_frames + window_frames must be in [1, %d]", LL_MAX_SLOTS);
-  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8) return fail(LL_ERR_INVALID, "unknown kv_dtype %d", kv_dtype);
+  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8 && kv_dtype != LL_KV_FP8)
+    return fail(LL_ERR_INVALID, "unknown kv_dtype %d", kv_dtype);
   const int64_t rows = int64_t(tokens_per_frame) * heads;
   if (slots * tokens_per_frame > kMaxRows || rows > kMaxRows) return fail(LL_ERR_INVALID, "cache too large");
-  const int64_t elt = kv_dtype == LL_KV_INT8 ? 1 : 2;
+  const bool quantised = kv_dtype != LL_KV_BF16;
+  const int64_t elt = quantised ? 1 : 2;
   auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
   const int64_t kv_bytes = round256(slots * rows * head_dim * elt);
-  const int64_t sc_bytes = kv_dtype == LL_KV_INT8 ? round256(slots * rows * 4) : 0;
+  const int64_t sc_bytes = quantised ? round256(slots * rows * 4) : 0;
   const double cache_total = double(layers) * 2.0 * double(kv_bytes + sc_bytes);
   if (cache_total > double(int64_t(1) << 46)) return fail(LL_ERR_INVALID, "cache too large (%.3g bytes)", cache_total);
 
@@ -254,7 +256,7 @@ ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void*
   p.ws_floats = c->ws_floats;
   p.cnt = c->cnt();
   p.n_cu = c->n_cu;
-  hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype == LL_KV_INT8, static_cast<hipStream_t>(stream));
+  hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -348,7 +350,7 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
   p.T = c->T;
   p.H = c->heads;
   p.D = c->head_dim;
-  p.kv_int8 = c->kv_dtype == LL_KV_INT8;
+  p.kv_fmt = c->kv_dtype;
   p.slotK = c->k(layer);
   p.slotV = c->v(layer);
   p.scK = c->ks(layer);

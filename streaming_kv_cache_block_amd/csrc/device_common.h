@@ -78,6 +78,31 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int byte0) {
   return pick_hi_hi(__builtin_bit_cast(uint32_t, f0), __builtin_bit_cast(uint32_t, f1));
 }
 
+// Exact OCP E4M3 -> bf16 of two codes (bytes byte0, byte0 + 1 of w; byte0 = 0 or 2):
+// every E4M3 value is a bf16 value, and a unit scale leaves it unchanged.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, int byte0) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = byte0 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Cache code formats (same values as the C ABI's kv_dtype).
+enum KvFmt : int { kKvBf16 = 0, kKvInt8 = 1, kKvFp8 = 2 };
+
+template <int FMT>
+__device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t w, int byte0) {
+  if constexpr (FMT == kKvFp8) return e4m3x2_to_bf16x2(w, byte0);
+  else return i8x2_to_bf16x2(w, byte0);
+}
+
+// Two fp32 values (|y| <= 448) -> two OCP E4M3 codes, round to nearest even, into the
+// low (hi_half = false) or high 16 bits of `old`.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float y0, float y1, uint32_t old, bool hi_half) {
+  return hi_half ? uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, int(old), true))
+                 : uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, int(old), false));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace ll

@@ -61,9 +61,10 @@ __device__ __forceinline__ int64_t slot_row(int m, int T, const int* plan) {
   return int64_t(plan[m / T]) * T + m % T;
 }
 
-// Epilogue of the fused recache: bf16 results, or their int8 quantisation
-//   a = max |x| over the (token, head) row, scale = a / 127,
-//   q = clamp(rint((x * 127) / a), -127, 127)   (0 for an all-zero row),
+// Epilogue of the fused recache: bf16 results, or their int8 / fp8 quantisation
+//   a = max |x| over the (token, head) row, scale = a / M,
+//   q = clamp(rint((x * M) / a), -M, M) with M = 127   (0 for an all-zero row),
+//   or the E4M3 rounding of clamp((x * M) / a, -M, M) with M = 448,
 // with the quotient correctly rounded as in the int8 cache writer (one IEEE reciprocal
 // per row and a Markstein FMA correction; plain division where the absmax is below
 // 2^-100 or above 2^120).  x is the bf16-rounded sum, exactly what a separate
@@ -122,6 +123,7 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
 #pragma unroll
       for (int b = 0; b < 4; ++b) am[b] = fmaxf(am[b], amax[wm][wn ^ 1][32 * b + r32]);
     }
+    constexpr float QM = EPI == 3 ? 448.0f : 127.0f;
     int8_t* base = static_cast<int8_t*>(z ? pc.slotV : pc.slotK);
     float* sc = z ? pc.scV : pc.scK;
 #pragma unroll
@@ -137,33 +139,44 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t packed = 0u;
+          if (a > 0.0f) {
+            float qq[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            int qi = 0;
-            if (a > 0.0f) {
-              const float n = x[b][aa][4 * i + j] * 127.0f;
-              float qq;
+            for (int j = 0; j < 4; ++j) {
+              const float n = x[b][aa][4 * i + j] * QM;
               if (plain) {
-                qq = n / a;
+                qq[j] = n / a;
               } else {
-                qq = n * y;
-                const float r = __builtin_fmaf(-a, qq, n);
-                qq = __builtin_fmaf(r, y, qq);
+                qq[j] = n * y;
+                const float r = __builtin_fmaf(-a, qq[j], n);
+                qq[j] = __builtin_fmaf(r, y, qq[j]);
               }
-              qi = int(fminf(fmaxf(__builtin_rintf(qq), -127.0f), 127.0f));
             }
-            packed |= (uint32_t(qi) & 0xffu) << (8 * j);
+            if constexpr (EPI == 3) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)   // saturate overflowed quotients; keep the sign of zero
+                qq[j] = __builtin_copysignf(fminf(fmaxf(qq[j], -448.0f), 448.0f), x[b][aa][4 * i + j]);
+              packed = f32x2_to_e4m3x2(qq[0], qq[1], 0u, false);
+              packed = f32x2_to_e4m3x2(qq[2], qq[3], packed, true);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int qi = int(fminf(fmaxf(__builtin_rintf(qq[j]), -127.0f), 127.0f));
+                packed |= (uint32_t(qi) & 0xffu) << (8 * j);
+              }
+            }
           }
           const int n_out = n0 + 64 * wn + 32 * aa + 8 * i + 4 * g;
           *reinterpret_cast<uint32_t*>(base + srow * N + n_out) = packed;
         }
       const int head = (n0 + 64 * wn) / pc.D;
-      if (g == 0 && (pc.D == 64 || wn == 0)) sc[srow * pc.H + head] = a / 127.0f;
+      if (g == 0 && (pc.D == 64 || wn == 0)) sc[srow * pc.H + head] = a / QM;
     }
   }
 }
 
-// EPI 0: plain [M][N] outputs; 1: bf16 rows into cache slots; 2: int8 rows + scales.
+// EPI 0: plain [M][N] outputs; 1: bf16 rows into cache slots; 2: int8 rows + scales;
+// 3: fp8 (E4M3) rows + scales.
 template <int EPI>
 __global__ __launch_bounds__(NT, 2) void proj_kernel(const ProjToCacheParams pc, int n_mt, int n_units) {
   const ProjParams& p = pc.proj;
@@ -290,7 +303,12 @@ hipError_t launch_kv_project(const ProjParams& p, hipStream_t s) {
 
 hipError_t launch_kv_project_to_cache(const ProjToCacheParams& p, hipStream_t s) {
   if (p.D != 64 && p.D != 128) return hipErrorInvalidValue;
-  return p.kv_int8 ? launch_proj<2>(p, s) : launch_proj<1>(p, s);
+  switch (p.kv_fmt) {
+    case kKvBf16: return launch_proj<1>(p, s);
+    case kKvInt8: return launch_proj<2>(p, s);
+    case kKvFp8: return launch_proj<3>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ll

@@ -11,8 +11,11 @@
 // int8 caches: each (token, head) row of D values is quantised on the fly
 //   a = max |x|, scale = a / 127, q = clamp(rint((x * 127) / a), -127, 127)
 // (every operation IEEE binary32, correctly rounded quotient, ties-to-even rounding;
-// x * 127 is exact for bf16 x).  LongLive-2.0 explainer, wmrh.cn, §15.2: the history
-// cache is stored in low precision to save memory and traffic.
+// x * 127 is exact for bf16 x).  fp8 caches: the same with M = 448 (largest finite
+// OCP E4M3 value) and the quotient, clamped to [-448, 448] (it exceeds that only when
+// x * 448 overflowed), rounded to E4M3 (nearest, ties to even) by the hardware
+// conversion.  LongLive-2.0 explainer, wmrh.cn, §15.2: the history cache is
+// stored in low precision to save memory and traffic.
 #include "device_common.h"
 #include "launch.h"
 
@@ -52,8 +55,9 @@ __global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams
 // Handbook of Floating-Point Arithmetic, ch. on division).  It needs no underflow or
 // overflow, so rows whose absmax is below 2^-100 or above 2^120 (where x * 127 may
 // overflow) use the plain IEEE division.
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParams p) {
+  constexpr float M = FMT == kKvFp8 ? 448.0f : 127.0f;
   constexpr int LPR = D / 8;
   constexpr int GROUPS = kThreads / LPR;
   constexpr int RPG = 4;
@@ -87,25 +91,40 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, LPR));
 
-    const float scale = a / 127.0f;
+    const float scale = a / M;
     uint32_t packed[2] = {0u, 0u};
     if (a > 0.0f) {
       const bool plain = a < 0x1p-100f || a > 0x1p+120f;
       const float y = 1.0f / a;
+      float qq[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float n = x[k] * 127.0f;   // exact for bf16 x
-        float qq;
+        const float n = x[k] * M;   // exact for bf16 x
         if (plain) {
-          qq = n / a;
+          qq[k] = n / a;
         } else {
-          qq = n * y;
-          const float r = __builtin_fmaf(-a, qq, n);
-          qq = __builtin_fmaf(r, y, qq);
+          qq[k] = n * y;
+          const float r = __builtin_fmaf(-a, qq[k], n);
+          qq[k] = __builtin_fmaf(r, y, qq[k]);
         }
-        const float t = __builtin_rintf(qq);
-        const int qi = int(fminf(fmaxf(t, -127.0f), 127.0f));
-        packed[k >> 2] |= (uint32_t(qi) & 0xffu) << (8 * (k & 3));
+      }
+      if constexpr (FMT == kKvFp8) {
+        // |quotient| <= 448 except when x * 448 overflowed (inf): saturate like the clamp.
+        // The FMA correction turns a -0 quotient into +0; the IEEE quotient has the sign
+        // of x (a > 0), and E4M3 keeps the sign of zero.
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qq[k] = __builtin_copysignf(fminf(fmaxf(qq[k], -448.0f), 448.0f), x[k]);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          packed[w] = f32x2_to_e4m3x2(qq[4 * w], qq[4 * w + 1], 0u, false);
+          packed[w] = f32x2_to_e4m3x2(qq[4 * w + 2], qq[4 * w + 3], packed[w], true);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int qi = int(fminf(fmaxf(__builtin_rintf(qq[k]), -127.0f), 127.0f));
+          packed[k >> 2] |= (uint32_t(qi) & 0xffu) << (8 * (k & 3));
+        }
       }
     }
     if (row < p.rows_per_frame) {
@@ -117,9 +136,9 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
 
 }  // namespace
 
-hipError_t launch_kv_write(const WriteParams& p, int D, bool kv_int8, hipStream_t s) {
+hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t s) {
   if (p.n <= 0) return hipSuccess;
-  if (!kv_int8) {
+  if (kv_fmt == kKvBf16) {
     const int64_t vecs = p.rows_per_frame * D * 2 / 16;
     const int64_t per_block = int64_t(kThreads) * kUnroll;
     dim3 grid(unsigned((vecs + per_block - 1) / per_block), unsigned(p.n), 2);
@@ -128,13 +147,11 @@ hipError_t launch_kv_write(const WriteParams& p, int D, bool kv_int8, hipStream_
   }
   const int rows_per_block = kThreads / (D / 8) * 4;
   dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
-  if (D == 128) {
-    hipLaunchKernelGGL(quant_frames_kernel<128>, grid, dim3(kThreads), 0, s, p);
-  } else if (D == 64) {
-    hipLaunchKernelGGL(quant_frames_kernel<64>, grid, dim3(kThreads), 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (D == 128 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<128, kKvInt8>), grid, dim3(kThreads), 0, s, p);
+  else if (D == 64 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<64, kKvInt8>), grid, dim3(kThreads), 0, s, p);
+  else if (D == 128 && kv_fmt == kKvFp8) hipLaunchKernelGGL((quant_frames_kernel<128, kKvFp8>), grid, dim3(kThreads), 0, s, p);
+  else if (D == 64 && kv_fmt == kKvFp8) hipLaunchKernelGGL((quant_frames_kernel<64, kKvFp8>), grid, dim3(kThreads), 0, s, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -50,9 +50,10 @@ struct Split {
 // Partial-result slots a split launch may use: blocks < CUs, three pieces at most.
 inline int64_t split_ws_floats(int D, int n_cu) { return split_slot_floats(D, 256) * 3 * int64_t(n_cu); }
 
-hipError_t launch_attention(const AttnParams& p, int D, bool kv_int8, hipStream_t s);
+// kv_fmt: 0 bf16 cache, 1 int8 codes, 2 fp8 (E4M3) codes (+ fp32 scales).
+hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t s);
 
-// Copy (bf16) or quantise (int8) whole frames of a [frames*T][H][D] bf16 tensor into
+// Copy (bf16) or quantise (int8 / fp8) whole frames of a [frames*T][H][D] bf16 tensor into
 // cache slots.  plan_src[i] is the frame index in the source tensor, plan_slot[i] the
 // destination slot, for i < n.
 struct WriteParams {
@@ -60,7 +61,7 @@ struct WriteParams {
   const uint16_t* srcV;
   void* dstK;           // slot array of the layer: [S+W][T][H][D]
   void* dstV;
-  float* dstKs;         // int8: [S+W][T][H]
+  float* dstKs;         // int8 / fp8: [S+W][T][H]
   float* dstVs;
   int64_t rows_per_frame;  // T*H
   int n;
@@ -68,7 +69,7 @@ struct WriteParams {
   int plan_slot[kMaxPlan];
 };
 
-hipError_t launch_kv_write(const WriteParams& p, int D, bool kv_int8, hipStream_t s);
+hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t s);
 
 // out[m][n] = sum_k h[m][k] * W[n][k] for W = W_K and W_V (bf16 in, fp32 sums,
 // bf16 out).  M rows, K = d_in (multiple of 64), N = d_out (multiple of 128).
@@ -84,16 +85,16 @@ struct ProjParams {
 hipError_t launch_kv_project(const ProjParams& p, hipStream_t s);
 
 // Projection whose epilogue writes straight into cache slots: output row m (frame
-// m / T, token m % T) goes to slot plan_slot[m / T]; N = H * D.  int8 caches get the
-// per-(token, head) quantisation of the bf16-rounded results (same bits as projecting,
-// then quantising the stored bf16 tensor).
+// m / T, token m % T) goes to slot plan_slot[m / T]; N = H * D.  int8 / fp8 caches get
+// the per-(token, head) quantisation of the bf16-rounded results (same bits as
+// projecting, then quantising the stored bf16 tensor).
 struct ProjToCacheParams {
   ProjParams proj;      // outK/outV unused
   int T, H, D;
-  bool kv_int8;
+  int kv_fmt;           // 0 bf16, 1 int8, 2 fp8
   void* slotK;          // layer slot arrays [S+W][T][H][D]
   void* slotV;
-  float* scK;           // int8: [S+W][T][H]
+  float* scK;           // int8 / fp8: [S+W][T][H]
   float* scV;
   int n_plan;
   int plan_slot[kMaxPlan];

@@ -64,10 +64,12 @@ def compare_attention(gpu_out, ref, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
     return mx, mn
 
 
-def check_slots(cache, layer, hist, kv_int8=False):
+def check_slots(cache, layer, hist, kv_int8=False, kv=None):
     """Slot->frame map equals the slot model; every occupied slot holds exactly the
-    bytes (or the int8 quantisation) of the frame it claims; the occupied frames are
-    the cached part of the visible set."""
+    bytes (or the int8 / fp8 quantisation) of the frame it claims; the occupied frames
+    are the cached part of the visible set."""
+    if kv is None:
+        kv = "int8" if kv_int8 else "bf16"
     sf = cache.slot_frames(layer)
     assert sf == hist.model.slot_frame, (sf, hist.model.slot_frame)
     assert cache.frames_seen(layer) == hist.f0
@@ -76,13 +78,20 @@ def check_slots(cache, layer, hist, kv_int8=False):
         if f < 0:
             continue
         kb, vb = hist(f)
-        if not kv_int8:
+        if kv == "bf16":
             assert np.array_equal(got["K"][s].view(np.uint16), kb), f"K slot {s} frame {f}"
             assert np.array_equal(got["V"][s].view(np.uint16), vb), f"V slot {s} frame {f}"
         else:
             for name, src in (("K", kb), ("V", vb)):
-                q, sc = quant.quantize(bf16.to_f32(src))
-                assert np.array_equal(got[name][s].view(np.int8), q), f"{name} codes slot {s} frame {f}"
+                if kv == "int8":
+                    q, sc = quant.quantize(bf16.to_f32(src))
+                    same = got[name][s].view(np.int8) == q
+                else:
+                    q, sc = quant.quantize_fp8(bf16.to_f32(src))
+                    same = got[name][s].view(np.uint8) == q
+                if not same.all():
+                    bad = np.argwhere(~same)[:4].tolist()
+                    raise AssertionError(f"{name} codes slot {s} frame {f}: {int((~same).sum())} differ, e.g. {bad}")
                 assert np.array_equal(got[name + "_scale"][s].view(np.uint32), sc.view(np.uint32)), \
                     f"{name} scales slot {s} frame {f}"
 

@@ -53,7 +53,7 @@ def test_create_rejects_invalid_arguments_before_touching_hip(L):
         (1, 12, 128, 1560, -1, 12, 0),     # negative sink
         (1, 12, 128, 1560, 0, 0, 0),       # no slots
         (1, 12, 128, 1560, 64, 65, 0),     # too many slots
-        (1, 12, 128, 1560, 3, 12, 7),      # dtype
+        (1, 12, 128, 1560, 3, 12, 3),      # dtype
         (1, 1 << 20, 128, 1 << 20, 3, 12, 0),  # too large
     ]
     for args in bad:
@@ -98,7 +98,7 @@ def test_missing_device_is_reported_not_crashed(L):
 
 def test_python_binding_rejects_unknown_dtype():
     with pytest.raises(ValueError):
-        ll.Cache(1, 2, 64, 16, 3, 6, kv_dtype="fp8")
+        ll.Cache(1, 2, 64, 16, 3, 6, kv_dtype="fp4")
 
 
 def _run_cli(lines):

@@ -1,7 +1,7 @@
 """GPU parity of the fused recache (projection whose epilogue writes the cache slots).
 
 ll_cache_recache_from_hidden must leave exactly the bytes that ll_kv_project
-followed by ll_cache_recache leaves (bf16 slots, or int8 codes and fp32 scales),
+followed by ll_cache_recache leaves (bf16 slots, or int8 / fp8 codes and fp32 scales),
 and those bytes must match the oracle's cache model fed the projected K/V.
 Shapes: ragged token counts (T not a multiple of the 256-token tile), head_dim 64
 (two heads per 128-output tile) and 128, caches that are not yet full and caches
@@ -73,11 +73,11 @@ def _case(torch, H, D, T, S, W, d_in, kv, appends, seed):
     b.recache_from_hidden(0, hd, wkd, wvd)
     _retained_equal(a, b, "fused vs project+recache")
     hist.recache(synth.to_bits(K).reshape(n * T, H, D), synth.to_bits(V).reshape(n * T, H, D))
-    check_slots(b, 0, hist, kv_int8=(kv == "int8"))
+    check_slots(b, 0, hist, kv=kv)
     return b, hist
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 @pytest.mark.parametrize("H,D,T,S,W,d_in,appends", [
     (2, 64, 33, 3, 6, 128, [3, 3]),            # not full: 6 of 9 slots, ragged tiles
     (2, 64, 33, 3, 6, 192, [3, 3, 3, 3, 3]),   # wrapped ring
@@ -89,7 +89,7 @@ def test_fused_recache_matches_project_then_recache(torch_gpu, kv, H, D, T, S, W
     _case(torch_gpu, H, D, T, S, W, d_in, kv, appends, seed=300 + H * 7 + T)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_fused_recache_full_size(torch_gpu, kv):
     cfg = configs.RECACHE
     _case(torch_gpu, cfg.heads, cfg.head_dim, cfg.tokens_per_frame, cfg.sink, cfg.window, cfg.hidden, kv,

@@ -42,17 +42,17 @@ def _prefill(cache, hist, cfg, layer, n_chunks, tag):
         hist.append(kb, vb)
 
 
-@pytest.mark.parametrize("kv_int8", [False, True])
-def test_steady_state_step(torch_gpu, kv_int8):
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_steady_state_step(torch_gpu, kv):
     cfg = configs.STEADY
-    if kv_int8:   # the int8 workload's window
+    if kv != "bf16":   # the low-bit workload's window
         cfg = configs.Workload(**{**cfg.__dict__, "window": configs.LONG_INT8.window, "kv_int8": True,
                                   "prefill_chunks": 9, "seed": configs.LONG_INT8.seed})
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
-    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8" if kv_int8 else "bf16")
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     hist = History(S, W, T)
     _prefill(cache, hist, cfg, 0, cfg.prefill_chunks, 100)
-    check_slots(cache, 0, hist, kv_int8=kv_int8)
+    check_slots(cache, 0, hist, kv=kv)
     f0 = hist.f0
     shape = (cfg.nq, H, D)
     rows = sample_rows(cfg.nq, T, seed=cfg.seed)
@@ -61,15 +61,15 @@ def test_steady_state_step(torch_gpu, kv_int8):
         out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
         t0 = time.time()
         if p == 0:
-            ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv_int8=kv_int8)
+            ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv)
             mx, mn = compare_attention(out, ref, f"pass {p} (all rows)")
         else:
-            ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv_int8=kv_int8, rows=rows)
+            ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv, rows=rows)
             mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"pass {p} (sampled rows)")
-        _log(f"steady int8={kv_int8} pass {p}: max-abs {mx:.2e} mean-abs {mn:.2e} oracle {time.time() - t0:.1f}s")
+        _log(f"steady kv={kv} pass {p}: max-abs {mx:.2e} mean-abs {mn:.2e} oracle {time.time() - t0:.1f}s")
     cache.append(0, synth.to_device(kc), synth.to_device(vc))
     hist.append(kc, vc)
-    check_slots(cache, 0, hist, kv_int8=kv_int8)
+    check_slots(cache, 0, hist, kv=kv)
 
 
 def test_projection_identity_and_small_integers_bit_exact(torch_gpu):

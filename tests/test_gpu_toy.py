@@ -11,7 +11,7 @@ import pytest
 
 import streaming_kv_cache_block_amd as ll
 import synth
-from oracle import attention, bf16, visibility
+from oracle import attention, bf16, quant, visibility
 from synth import configs
 
 from helpers import History, check_slots, compare_attention
@@ -34,9 +34,9 @@ def _chunk_inputs(cfg, k, p, sigma=None):
     return tuple(synth.normal_bf16(shape, s, cfg.seed, t, 0, k, p) for t in range(3))
 
 
-def _rollout(torch, cfg, kv_int8=False, chunk_sizes=None, check_every_pass=True):
+def _rollout(torch, cfg, kv="bf16", chunk_sizes=None, check_every_pass=True):
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
-    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8" if kv_int8 else "bf16")
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     hist = History(S, W, T)
     for k in range(cfg.chunks):
         f0 = hist.f0
@@ -44,11 +44,11 @@ def _rollout(torch, cfg, kv_int8=False, chunk_sizes=None, check_every_pass=True)
             q, kc, vc = _chunk_inputs(cfg, k, p)
             out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
             if check_every_pass or p == cfg.passes - 1:
-                ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv_int8=kv_int8)
+                ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv)
                 compare_attention(out, ref, f"chunk {k} pass {p}")
         cache.append(0, synth.to_device(kc), synth.to_device(vc))
         hist.append(kc, vc)
-        check_slots(cache, 0, hist, kv_int8=kv_int8)
+        check_slots(cache, 0, hist, kv=kv)
     return cache, hist
 
 
@@ -57,7 +57,11 @@ def test_toy_rollout_bf16(torch_gpu):
 
 
 def test_toy_rollout_int8(torch_gpu):
-    _rollout(torch_gpu, configs.TOY, kv_int8=True)
+    _rollout(torch_gpu, configs.TOY, kv="int8")
+
+
+def test_toy_rollout_fp8(torch_gpu):
+    _rollout(torch_gpu, configs.TOY, kv="fp8")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -116,18 +120,19 @@ def test_append_longer_than_window_and_sink_only(torch_gpu):
             compare_attention(out, ref, f"S={S} W={W} step {j}")
 
 
-@pytest.mark.parametrize("kv_int8", [False, True])
-def test_recache_overwrites_every_slot(torch_gpu, kv_int8):
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_recache_overwrites_every_slot(torch_gpu, kv):
     """Prefill with NaN K/V, recache with finite tensors: no stale (NaN) slot may
     survive, the bytes must be exactly the recache blocks, and attention must match
     the oracle fed the recache tensors."""
     torch = torch_gpu
     T, H, D, S, W, C = 32, 2, 128, 3, 6, 3
-    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8" if kv_int8 else "bf16")
+    kv_int8 = kv != "bf16"
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     hist = History(S, W, T)
     nan = np.full((C * T, H, D), 0x7FC0, dtype=np.uint16)   # bf16 quiet NaN
     for k in range(5):
-        if kv_int8:   # int8 codes of NaN rows are undefined; poison through the chunk path
+        if kv_int8:   # codes of NaN rows are undefined; poison through the chunk path
             kb = synth.normal_bf16((C * T, H, D), 1.0, 90, k, 0)
             cache.append(0, synth.to_device(kb), synth.to_device(kb))
             hist.append(kb, kb)
@@ -139,7 +144,7 @@ def test_recache_overwrites_every_slot(torch_gpu, kv_int8):
     V_all = synth.normal_bf16((n * T, H, D), 1.0, 91, 1)
     cache.recache(0, synth.to_device(K_all), synth.to_device(V_all))
     hist.recache(K_all, V_all)
-    check_slots(cache, 0, hist, kv_int8=kv_int8)
+    check_slots(cache, 0, hist, kv=kv)
     got = cache.slot_bytes(0)
     if not kv_int8:
         assert not np.isnan(bf16.to_f32(got["K"].view(np.uint16))).any()
@@ -148,7 +153,7 @@ def test_recache_overwrites_every_slot(torch_gpu, kv_int8):
     kc = synth.normal_bf16((C * T, H, D), 1.0, 92, 1)
     vc = synth.normal_bf16((C * T, H, D), 1.0, 92, 2)
     out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
-    ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv_int8=kv_int8)
+    ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv=kv)
     compare_attention(out, ref, "after recache")
     # wrong frame count is a state error, not a launch
     with pytest.raises(ll.LLError) as e:
@@ -189,16 +194,26 @@ def test_empty_cache_first_chunk_and_ragged_lengths(torch_gpu):
             hist.append(kc, vc)
 
 
-def test_int8_quantisation_edge_rows_bit_exact(torch_gpu):
-    """Rows built to hit every branch of the int8 rule: exact .5 ties, +-absmax, all-zero
-    rows, a single non-zero element, tiny (~2^-110) and huge (~2^121, x*127 overflows)
-    magnitudes, and ordinary Gaussian rows; codes and scales must equal the oracle's."""
+@pytest.mark.parametrize("kv", ["int8", "fp8"])
+def test_quantisation_edge_rows_bit_exact(torch_gpu, kv):
+    """Rows built to hit every branch of the int8 / fp8 rule: exact ties (.5 for int8;
+    E4M3 midpoints, normal and subnormal, for fp8 with absmax 448 so that the quotient
+    is the value itself), +-absmax, all-zero rows, a single non-zero element, tiny
+    (~2^-110) and huge (~2^121, x*M overflows) magnitudes, and ordinary Gaussian rows;
+    codes and scales must equal the oracle's."""
     T, H, D, S, W = 24, 2, 128, 2, 3
     rng = np.random.default_rng(21)
     x = rng.standard_normal((T, H, D)).astype(np.float32)
     ties = np.zeros(D, dtype=np.float32)
-    ties[:8] = [254.0, 1.0, 3.0, 5.0, -1.0, -3.0, -5.0, -254.0]
-    ties[8:] = (2 * rng.integers(-60, 60, D - 8) + 1).astype(np.float32)
+    if kv == "int8":
+        ties[:8] = [254.0, 1.0, 3.0, 5.0, -1.0, -3.0, -5.0, -254.0]
+        ties[8:] = (2 * rng.integers(-60, 60, D - 8) + 1).astype(np.float32)
+    else:
+        v = quant.e4m3_values()
+        mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)          # 126 midpoints, bf16-exact
+        ties[0] = 448.0
+        ties[1:1 + len(mids)] = mids * np.where(np.arange(len(mids)) % 2, -1, 1).astype(np.float32)
+        ties[127] = -448.0
     for t in range(T):
         kind = t % 8
         if kind == 1:
@@ -216,11 +231,12 @@ def test_int8_quantisation_edge_rows_bit_exact(torch_gpu):
             x[t, 0] *= np.float32(2.0 ** -20)
             x[t, 1] *= np.float32(2.0 ** 20)
     frames = synth.f32_to_bf16_bits(x)
-    cache = ll.Cache(1, H, D, T, S, W, kv_dtype="int8")
+    assert (bf16.to_f32(synth.f32_to_bf16_bits(ties)) == ties).all()   # the tie row is bf16-exact
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     hist = History(S, W, T)
     for k in range(4):
         kb = frames if k % 2 == 0 else synth.f32_to_bf16_bits(-x)
         vb = synth.f32_to_bf16_bits(x[::-1].copy())
         cache.append(0, synth.to_device(kb), synth.to_device(vb))
         hist.append(kb, vb)
-        check_slots(cache, 0, hist, kv_int8=True)
+        check_slots(cache, 0, hist, kv=kv)
