@@ -92,6 +92,36 @@ ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_fr
                           int sink_frames, int window_frames, int kv_dtype,
                           ll_cache **out);
 
+/*
+ * ll_cache_create_shots -- a cache with a shot sink as well as the global sink.
+ * [LL2-wmrh §16]: multi-shot generation keeps a global-level sink that every shot
+ * attends to and a shot-level sink holding the current shot's own context.  Reading
+ * adopted (the page names the two levels only): the global sink is the first
+ * sink_frames frames of the video, the shot sink the first shot_sink_frames frames of
+ * the current shot (ll_cache_begin_shot), and a chunk starting at f0 in the shot that
+ * started at fs sees
+ *     {f < min(S, f0)} U {fs <= f < min(fs + Ss, f0)} U {max(0, f0-W) <= f < f0}
+ * plus its own chunk.  Slots: [0, S) global sink, [S, S+Ss) shot sink, [S+Ss, S+Ss+W)
+ * window ring; a shot-sink frame is stored in its shot slot and its ring slot.
+ * ll_cache_create is this function with shot_sink_frames = 0.
+ *   shot_sink_frames  Ss >= 0, 1 <= S + Ss + W <= LL_MAX_SLOTS
+ * Other arguments, memory and errors as ll_cache_create.
+ */
+ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_per_frame,
+                                int sink_frames, int shot_sink_frames, int window_frames,
+                                int kv_dtype, ll_cache **out);
+
+/*
+ * ll_cache_begin_shot -- the next frame appended to `layer` starts a new shot: fs = f0,
+ * and the previous shot's sink is no longer visible (its shot slots are marked empty;
+ * frames of it still inside the window stay visible through the window).  Host
+ * bookkeeping only, no device work.  Errors: LL_ERR_INVALID.
+ */
+ll_status ll_cache_begin_shot(ll_cache *c, int layer);
+
+/* First frame of the current shot of `layer` (0 until ll_cache_begin_shot). */
+ll_status ll_cache_shot_start(const ll_cache *c, int layer, int64_t *fs);
+
 /* Free the cache's device memory and the handle (NULL is accepted).  The caller
  * must make sure no enqueued work still uses it. */
 void ll_cache_destroy(ll_cache *c);
@@ -140,7 +170,9 @@ ll_status ll_attn_sink_window(ll_cache *c, int layer, const void *Q, const void 
  * unchanged.
  *   K_all, V_all  [n_frames*T][heads][head_dim] bf16
  *   n_frames      must equal min(f0, S+W) (else LL_ERR_STATE; 0 frames cached is
- *                 LL_ERR_STATE too)
+ *                 LL_ERR_STATE too); with a shot sink, the number of retained
+ *                 frames (the cached visible set), in ascending frame order; a
+ *                 frame held in two slots gets its block in both
  * Errors: LL_ERR_INVALID, LL_ERR_STATE, LL_ERR_HIP.
  */
 ll_status ll_cache_recache(ll_cache *c, int layer, const void *K_all, const void *V_all,
@@ -193,13 +225,13 @@ ll_status ll_cache_recache_from_hidden(ll_cache *c, int layer, const void *h, co
 /* Frames appended to `layer` so far (f0). */
 ll_status ll_cache_frames_seen(const ll_cache *c, int layer, int64_t *f0);
 
-/* For each of the S+W slots of `layer`, the frame it holds, or -1 if empty.
+/* For each of the S+Ss+W slots of `layer`, the frame it holds, or -1 if empty.
  * frame_of_slot must have room for S+W entries (host memory). */
 ll_status ll_cache_slot_frames(const ll_cache *c, int layer, int64_t *frame_of_slot);
 
 /* Device pointers of `layer`'s slot arrays (read them after synchronising):
- *   K, V        [S+W][T][heads][head_dim], bf16, int8 or E4M3 bytes (kv_dtype)
- *   K_scale, V_scale  [S+W][T][heads] fp32 for int8 / fp8 caches, NULL for bf16
+ *   K, V        [S+Ss+W][T][heads][head_dim], bf16, int8 or E4M3 bytes (kv_dtype)
+ *   K_scale, V_scale  [S+Ss+W][T][heads] fp32 for int8 / fp8 caches, NULL for bf16
  * Any output pointer may be NULL. */
 ll_status ll_cache_slot_view(const ll_cache *c, int layer, void **K, void **V,
                              void **K_scale, void **V_scale);

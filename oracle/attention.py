@@ -98,7 +98,7 @@ def _widen(bits, dtype):
 
 
 def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
-                    kv_int8=False, rows=None, dtype=np.float32, kv=None):
+                    kv_int8=False, rows=None, dtype=np.float32, kv=None, shot=None):
     """Attention of one chunk over V(f0), straight from the definition.
 
     Q, K_chunk, V_chunk: uint16 bf16 bits, shape [C*T][H][D] (own chunk).
@@ -110,6 +110,8 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
         format (oracle.quant) and are dequantised before use; own-chunk K/V
         are never quantised.  kv_int8=True is the same as kv="int8".
     rows: optional list of query rows to compute (sampled checks).
+    shot: optional (Ss, fs): a shot sink of the first Ss frames of the shot that
+        starts at frame fs (visibility.visible_frames_shots).
     Returns O [len(rows) or C*T][H][D] in ``dtype``.
 
     Keys are laid out frame by frame in ascending frame order; the mask is
@@ -126,7 +128,8 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
     if nq_all % T:
         raise ValueError("chunk length is not a whole number of frames")
     C = nq_all // T
-    fmask = _vis.frame_mask(f0, C, S, W, f0 + C)
+    Ss, fs = shot if shot is not None else (0, 0)
+    fmask = _vis.frame_mask(f0, C, S, W, f0 + C, Ss, fs)
     Ks, Vs = [], []
     for f in range(f0 + C):
         if not fmask[f]:

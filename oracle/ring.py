@@ -30,52 +30,81 @@ Each slot records which frame it holds (``slot_frame``, -1 = empty) and a
 caller-defined token for where its bytes came from (``slot_src``), so tests
 can compare GPU slot bytes with the bytes of the frame the model says are
 there.
+
+Shot sinks (LongLive-2.0 explainer, wmrh.cn, §16; reading in visibility.py):
+with Ss > 0 the layer has S + Ss + W slots: [0, S) global sink, [S, S + Ss)
+shot sink, [S + Ss, S + Ss + W) window ring.  A frame f >= S of the current
+shot's first Ss frames (fs <= f < fs + Ss) is written to its shot slot
+S + (f - fs) AND to its ring slot S + Ss + (f - S) mod W; ``begin_shot()``
+sets fs = f0 and empties the shot slots.  The frames held are then exactly
+the cached part of V(f0; fs); a frame held twice is one frame.  Recache
+takes the retained frames in ascending order and writes block idx to every
+slot holding frame idx.
 """
 
 
 class RingModel:
-    def __init__(self, S: int, W: int):
-        if S < 0 or W < 0 or S + W == 0:
-            raise ValueError("need S >= 0, W >= 0, S + W > 0")
-        self.S, self.W = S, W
+    def __init__(self, S: int, W: int, Ss: int = 0):
+        if S < 0 or W < 0 or Ss < 0 or S + Ss + W == 0:
+            raise ValueError("need S, Ss, W >= 0 and S + Ss + W > 0")
+        self.S, self.W, self.Ss = S, W, Ss
         self.f0 = 0
-        self.slot_frame = [-1] * (S + W)
-        self.slot_src = [None] * (S + W)
+        self.fs = 0
+        self.slot_frame = [-1] * (S + Ss + W)
+        self.slot_src = [None] * (S + Ss + W)
+
+    def slots_of(self, f: int) -> list:
+        """Slots that store frame f (given the current shot)."""
+        if f < self.S:
+            return [f]
+        out = []
+        if self.fs <= f < self.fs + self.Ss:
+            out.append(self.S + (f - self.fs))
+        if self.W > 0:
+            out.append(self.S + self.Ss + (f - self.S) % self.W)
+        return out
 
     def slot_of(self, f: int):
-        if f < self.S:
-            return f
-        if self.W == 0:
-            return None
-        return self.S + (f - self.S) % self.W
+        """The single slot of frame f when there is no shot sink (None if dropped)."""
+        s = self.slots_of(f)
+        if self.Ss:
+            raise ValueError("slot_of: frames may have two slots with a shot sink")
+        return s[0] if s else None
+
+    def begin_shot(self):
+        self.fs = self.f0
+        for s in range(self.S, self.S + self.Ss):
+            self.slot_frame[s] = -1
+            self.slot_src[s] = None
 
     def append(self, n: int, src_of_frame=lambda f: f):
         if n <= 0:
             raise ValueError("append needs n > 0")
         for i in range(n):
             f = self.f0 + i
-            s = self.slot_of(f)
-            if s is None:
-                continue
-            self.slot_frame[s] = f
-            self.slot_src[s] = src_of_frame(f)
+            for s in self.slots_of(f):
+                self.slot_frame[s] = f
+                self.slot_src[s] = src_of_frame(f)
         self.f0 += n
 
     def retained_frames(self) -> list:
-        """Logical recache order: sink ascending, then window oldest -> newest."""
-        sink = list(range(0, min(self.S, self.f0)))
-        window = list(range(max(self.S, self.f0 - self.W), self.f0))
-        return sink + window
+        """Logical recache order: the cached visible frames ascending (sink, shot sink,
+        then window oldest -> newest)."""
+        sink = set(range(0, min(self.S, self.f0)))
+        shot = set(range(max(self.S, self.fs), min(self.fs + self.Ss, self.f0)))
+        window = set(range(max(self.S, self.f0 - self.W), self.f0))
+        return sorted(sink | shot | window)
 
     def recache(self, n: int, src_of_block=lambda idx: idx):
         frames = self.retained_frames()
-        if n != len(frames) or n != min(self.f0, self.S + self.W):
-            raise ValueError("recache: n must equal min(f0, S + W)")
+        if n != len(frames):
+            raise ValueError("recache: n must equal the number of retained frames")
         for idx, f in enumerate(frames):
-            s = self.slot_of(f)
-            if self.slot_frame[s] != f:
+            held = [s for s, g in enumerate(self.slot_frame) if g == f]
+            if not held:
                 raise AssertionError("ring model inconsistent")
-            self.slot_src[s] = src_of_block(idx)
+            for s in held:
+                self.slot_src[s] = src_of_block(idx)
 
     def occupied_frames(self) -> list:
-        return sorted(f for f in self.slot_frame if f >= 0)
+        return sorted(set(f for f in self.slot_frame if f >= 0))

@@ -28,6 +28,17 @@ frames is
           U {f : max(0, f0 - W) <= f < f0}
           U {f0, ..., f0 + C - 1}.
 
+Multi-shot sinks (LongLive-2.0 explainer, wmrh.cn, §16): a global sink that every
+shot attends to and a shot sink that keeps the current shot's own early context.
+Reading adopted (the page names the two levels only): the global sink is the
+first S frames of the video as above; the shot sink is the first Ss frames of
+the current shot, which starts at frame fs (fs <= f0); a chunk sees their union
+with the window and its own chunk:
+
+    V(f0; fs) = V(f0) U {f : fs <= f < min(fs + Ss, f0)}.
+
+With Ss = 0 (or a shot sink inside the global sink) this is V(f0).
+
 This module never refers to slots, rings or physical positions.
 """
 
@@ -44,15 +55,23 @@ def visible_frames(f0: int, C: int, S: int, W: int) -> list:
     return sorted(sink | window | own)
 
 
-def cached_visible_frames(f0: int, S: int, W: int) -> list:
-    """The history part of V(f0): sink frames plus the last W frames before f0."""
-    return visible_frames(f0, 0, S, W)
+def visible_frames_shots(f0: int, C: int, S: int, Ss: int, W: int, fs: int) -> list:
+    """Sorted frames visible to the chunk [f0, f0+C) in the shot that starts at fs."""
+    if Ss < 0 or fs < 0 or fs > f0:
+        raise ValueError("need Ss >= 0 and 0 <= fs <= f0")
+    shot = set(range(fs, min(fs + Ss, f0)))
+    return sorted(set(visible_frames(f0, C, S, W)) | shot)
 
 
-def frame_mask(f0: int, C: int, S: int, W: int, n_frames: int) -> np.ndarray:
-    """Boolean mask over frames [0, n_frames): True where the frame is in V(f0)."""
+def cached_visible_frames(f0: int, S: int, W: int, Ss: int = 0, fs: int = 0) -> list:
+    """The history part of V(f0) (with a shot sink of Ss frames from fs, if any)."""
+    return visible_frames_shots(f0, 0, S, Ss, W, fs)
+
+
+def frame_mask(f0: int, C: int, S: int, W: int, n_frames: int, Ss: int = 0, fs: int = 0) -> np.ndarray:
+    """Boolean mask over frames [0, n_frames): True where the frame is in V(f0; fs)."""
     m = np.zeros(n_frames, dtype=bool)
-    for f in visible_frames(f0, C, S, W):
+    for f in visible_frames_shots(f0, C, S, Ss, W, fs):
         if f < n_frames:
             m[f] = True
     return m

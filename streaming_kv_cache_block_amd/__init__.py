@@ -28,7 +28,7 @@ MAX_SLOTS = 128
 EXPORTS = [
     "ll_cache_create", "ll_cache_destroy", "ll_cache_append", "ll_attn_sink_window",
     "ll_cache_recache", "ll_cache_recache_window", "ll_kv_project", "ll_cache_recache_from_hidden",
-    "ll_cache_frames_seen",
+    "ll_cache_create_shots", "ll_cache_begin_shot", "ll_cache_shot_start", "ll_cache_frames_seen",
     "ll_cache_slot_frames", "ll_cache_slot_view", "ll_last_error",
 ]
 
@@ -54,6 +54,9 @@ def lib():
     vp, i32, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)
     sig = {
         "ll_cache_create": [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(vp)],
+        "ll_cache_create_shots": [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(vp)],
+        "ll_cache_begin_shot": [vp, i32],
+        "ll_cache_shot_start": [vp, i32, i64p],
         "ll_cache_destroy": [vp],
         "ll_cache_append": [vp, i32, vp, vp, i32, vp],
         "ll_attn_sink_window": [vp, i32, vp, vp, vp, i32, vp, vp],
@@ -108,17 +111,17 @@ def _stream(stream):
 class Cache:
     """Per-layer sink + window KV cache living in device memory."""
 
-    def __init__(self, layers, heads, head_dim, tokens_per_frame, sink, window, kv_dtype="bf16"):
+    def __init__(self, layers, heads, head_dim, tokens_per_frame, sink, window, kv_dtype="bf16", shot_sink=0):
         self.layers, self.heads, self.head_dim = layers, heads, head_dim
-        self.T, self.S, self.W = tokens_per_frame, sink, window
+        self.T, self.S, self.W, self.Ss = tokens_per_frame, sink, window, shot_sink
         self.kv_dtype = kv_dtype
         if kv_dtype not in _KV_NAMES and kv_dtype not in _KV_NAMES.values():
             raise ValueError(f"kv_dtype must be 'bf16', 'int8' or 'fp8', got {kv_dtype!r}")
         dt = _KV_NAMES.get(kv_dtype, kv_dtype)
         self.kv_code = dt
         h = ctypes.c_void_p()
-        _check(lib().ll_cache_create(layers, heads, head_dim, tokens_per_frame, sink, window, dt,
-                                     ctypes.byref(h)))
+        _check(lib().ll_cache_create_shots(layers, heads, head_dim, tokens_per_frame, sink, shot_sink, window, dt,
+                                           ctypes.byref(h)))
         self._h = h
 
     def close(self):
@@ -165,13 +168,21 @@ class Cache:
         _check(lib().ll_cache_recache_from_hidden(self._h, layer, _ptr(h), _ptr(W_K), _ptr(W_V),
                                                   self._frames(h, n_frames), h.shape[1], _stream(stream)))
 
+    def begin_shot(self, layer):
+        _check(lib().ll_cache_begin_shot(self._h, layer))
+
+    def shot_start(self, layer):
+        v = ctypes.c_int64()
+        _check(lib().ll_cache_shot_start(self._h, layer, ctypes.byref(v)))
+        return v.value
+
     def frames_seen(self, layer):
         v = ctypes.c_int64()
         _check(lib().ll_cache_frames_seen(self._h, layer, ctypes.byref(v)))
         return v.value
 
     def slot_frames(self, layer):
-        arr = (ctypes.c_int64 * (self.S + self.W))()
+        arr = (ctypes.c_int64 * (self.S + self.Ss + self.W))()
         _check(lib().ll_cache_slot_frames(self._h, layer, arr))
         return list(arr)
 
@@ -191,7 +202,7 @@ class Cache:
         import torch
         torch.cuda.synchronize()
         kp, vp, ksp, vsp = self.slot_view(layer)
-        slots = self.S + self.W
+        slots = self.S + self.Ss + self.W
         elt = 1 if self.kv_code != LL_KV_BF16 else 2
         nbytes = slots * self.T * self.heads * self.head_dim * elt
         out = {"K": _d2h(kp, nbytes).reshape(slots, self.T, self.heads, self.head_dim * elt),

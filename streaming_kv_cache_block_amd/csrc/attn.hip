@@ -85,20 +85,6 @@ struct TileInfo {
   int cnt;    // valid rows in the tile (1..BN)
 };
 
-__device__ __forceinline__ TileInfo tile_info(int j, int n1, int ncache, int nq) {
-  TileInfo t;
-  if (j < n1) {
-    t.seg = 0;
-    t.start = j * BN;
-    t.cnt = min(BN, ncache - t.start);
-  } else {
-    t.seg = 1;
-    t.start = (j - n1) * BN;
-    t.cnt = min(BN, nq - t.start);
-  }
-  return t;
-}
-
 // bf16 tile: every wave copies its share of rows straight into LDS.  Rows past the
 // segment end re-read the last valid row (its scores are masked to -inf and its
 // values then get probability 0, so the data only has to be finite).
@@ -194,39 +180,63 @@ struct QTile {
   }
 };
 
-// Order of the key tiles: the (at most two) partial tiles -- the last tile of each
-// segment -- come first, so that the long run of full tiles after them carries no
-// masking code.  Softmax attention does not depend on the order of its keys.
+// Order of the key tiles.  The keys are the cached runs (up to kMaxRuns runs of rows of
+// the slot array) and the own chunk; each is tiled on its own, so only the last tile of
+// each may be partial.  The partial tiles come first, so that the long stretch of full
+// tiles after them carries no masking code; then the full cache tiles run by run, then
+// the full own-chunk tiles.  Softmax attention does not depend on the order of its keys.
+// (All loops are unrolled over the run count so the tables stay in scalar registers.)
 struct TileOrder {
-  int n1, n2, np1, np2, ncache, nq;
-  __device__ TileOrder(int ncache_, int nq_) : ncache(ncache_), nq(nq_) {
-    n1 = (ncache + BN - 1) / BN;
-    n2 = (nq + BN - 1) / BN;
-    np1 = (ncache % BN) != 0;
-    np2 = (nq % BN) != 0;
+  int r0[kMaxRuns], rn[kMaxRuns], fc[kMaxRuns];   // first row, rows, full tiles per run
+  int nq, np, nfc, pmask;   // own rows, partial tiles, full cache tiles, runs with a partial tile
+  __device__ explicit TileOrder(const AttnParams& p) : nq(p.nq), np(0), nfc(0), pmask(0) {
+#pragma unroll
+    for (int k = 0; k < kMaxRuns; ++k) {
+      r0[k] = k < p.nrun ? p.run_row0[k] : 0;
+      rn[k] = k < p.nrun ? p.run_rows[k] : 0;
+      fc[k] = rn[k] / BN;
+      nfc += fc[k];
+      if (rn[k] % BN) {
+        pmask |= 1 << k;
+        ++np;
+      }
+    }
+    if (nq % BN) ++np;
   }
-  __device__ int npart() const { return np1 + np2; }
-  __device__ int full1_end() const { return np1 + np2 + n1 - np1; }   // end of full cache tiles
-  __device__ int total() const { return n1 + n2; }
+  __device__ int npart() const { return np; }
+  __device__ int full1_end() const { return np + nfc; }   // end of the full cache tiles
+  __device__ int total() const { return np + nfc + nq / BN; }
   __device__ TileInfo at(int j) const {
     TileInfo t;
-    if (j < np1 + np2) {
-      if (j == 0 && np1) {
-        t.seg = 0;
-        t.start = (n1 - 1) * BN;
-        t.cnt = ncache - t.start;
-      } else {
-        t.seg = 1;
-        t.start = (n2 - 1) * BN;
-        t.cnt = nq - t.start;
-      }
-    } else if (j < full1_end()) {
+    if (j < np) {   // the j-th partial tile: runs in order, then the own chunk
+      t.seg = 1;
+      t.start = nq / BN * BN;
+      t.cnt = nq % BN;
+      int seen = 0;
+#pragma unroll
+      for (int k = 0; k < kMaxRuns; ++k)
+        if ((pmask >> k) & 1) {
+          if (seen == j) {
+            t.seg = 0;
+            t.start = r0[k] + fc[k] * BN;
+            t.cnt = rn[k] - fc[k] * BN;
+          }
+          ++seen;
+        }
+    } else if (j < np + nfc) {
+      const int jj = j - np;
       t.seg = 0;
-      t.start = (j - np1 - np2) * BN;
+      t.start = 0;
       t.cnt = BN;
+      int base = 0;
+#pragma unroll
+      for (int k = 0; k < kMaxRuns; ++k) {
+        if (jj >= base && jj < base + fc[k]) t.start = r0[k] + (jj - base) * BN;
+        base += fc[k];
+      }
     } else {
       t.seg = 1;
-      t.start = (j - full1_end()) * BN;
+      t.start = (j - np - nfc) * BN;
       t.cnt = BN;
     }
     return t;
@@ -553,7 +563,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   Attn<D, NQB, NW, KV8> A;
   A.init_offsets(lane);
 
-  const TileOrder order(p.ncache, p.nq);
+  const TileOrder order(p);
   const int ntiles = order.total();
   uint32_t loff[Geo<D, NW>::DMA_PER_WAVE];
 #pragma unroll
@@ -725,7 +735,8 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   Split sp{};
   sp.n_qtiles = (p.nq + rows - 1) / rows;
   sp.B = sp.n_qtiles * p.H;
-  sp.J = (p.ncache + BN - 1) / BN + (p.nq + BN - 1) / BN;
+  sp.J = (p.nq + BN - 1) / BN;
+  for (int k = 0; k < p.nrun; ++k) sp.J += (p.run_rows[k] + BN - 1) / BN;
   sp.ws = p.ws;
   sp.cnt = p.cnt;
   // Split when the blocks leave CUs idle, every XCD has at least as many blocks as spare

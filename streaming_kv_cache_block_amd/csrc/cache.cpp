@@ -25,7 +25,7 @@
 static_assert(LL_MAX_SLOTS == ll::kMaxPlan, "plan table size must match LL_MAX_SLOTS");
 
 struct ll_cache {
-  int layers = 0, heads = 0, head_dim = 0, T = 0, S = 0, W = 0;
+  int layers = 0, heads = 0, head_dim = 0, T = 0, S = 0, Ss = 0, W = 0;
   int kv_dtype = LL_KV_BF16;
   int device = -1;
   int64_t rows_per_frame = 0;   // T * heads
@@ -36,7 +36,10 @@ struct ll_cache {
   int64_t ws_floats = 0;
   void* mem = nullptr;
   std::vector<int64_t> f0;
+  std::vector<int64_t> fs;      // first frame of the current shot (shot sink)
   std::vector<std::vector<int64_t>> slot_frame;
+
+  ll::Layout layout() const { return ll::Layout{S, Ss, W}; }
 
   char* base() const { return static_cast<char*>(mem); }
   void* k(int l) const { return base() + (size_t(2) * l) * kv_bytes; }
@@ -142,16 +145,23 @@ const char* ll_last_error(void) { return g_err.c_str(); }
 
 ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_frame, int sink_frames,
                           int window_frames, int kv_dtype, ll_cache** out) {
+  return ll_cache_create_shots(layers, heads, head_dim, tokens_per_frame, sink_frames, 0, window_frames, kv_dtype,
+                               out);
+}
+
+ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_per_frame, int sink_frames,
+                                int shot_sink_frames, int window_frames, int kv_dtype, ll_cache** out) {
   if (!out) return fail(LL_ERR_INVALID, "out is NULL");
   *out = nullptr;
   if (layers < 1) return fail(LL_ERR_INVALID, "layers must be >= 1");
   if (heads < 1) return fail(LL_ERR_INVALID, "heads must be >= 1");
   if (head_dim != 64 && head_dim != 128) return fail(LL_ERR_INVALID, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (tokens_per_frame < 1) return fail(LL_ERR_INVALID, "tokens_per_frame must be >= 1");
-  if (sink_frames < 0 || window_frames < 0) return fail(LL_ERR_INVALID, "sink_frames and window_frames must be >= 0");
-  const int64_t slots = int64_t(sink_frames) + window_frames;
+  if (sink_frames < 0 || window_frames < 0 || shot_sink_frames < 0)
+    return fail(LL_ERR_INVALID, "sink_frames, shot_sink_frames and window_frames must be >= 0");
+  const int64_t slots = int64_t(sink_frames) + shot_sink_frames + window_frames;
   if (slots < 1 || slots > LL_MAX_SLOTS)
-    return fail(LL_ERR_INVALID, "sink_frames + window_frames must be in [1, %d]", LL_MAX_SLOTS);
+    return fail(LL_ERR_INVALID, "sink_frames + shot_sink_frames + window_frames must be in [1, %d]", LL_MAX_SLOTS);
   if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8 && kv_dtype != LL_KV_FP8)
     return fail(LL_ERR_INVALID, "unknown kv_dtype %d", kv_dtype);
   const int64_t rows = int64_t(tokens_per_frame) * heads;
@@ -193,6 +203,7 @@ ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_fr
   c->head_dim = head_dim;
   c->T = tokens_per_frame;
   c->S = sink_frames;
+  c->Ss = shot_sink_frames;
   c->W = window_frames;
   c->kv_dtype = kv_dtype;
   c->device = dev;
@@ -204,6 +215,7 @@ ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_fr
   c->ws_floats = ws_floats;
   c->mem = mem;
   c->f0.assign(size_t(layers), 0);
+  c->fs.assign(size_t(layers), 0);
   c->slot_frame.assign(size_t(layers), std::vector<int64_t>(size_t(slots), -1));
   *out = c;
   return ok();
@@ -222,7 +234,7 @@ ll_status ll_cache_append(ll_cache* c, int layer, const void* K, const void* V, 
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
   const int64_t f0 = c->f0[size_t(layer)];
-  const std::vector<ll::WriteEntry> plan = ll::append_plan(f0, n_frames, c->S, c->W);
+  const std::vector<ll::WriteEntry> plan = ll::append_plan(f0, n_frames, c->layout(), c->fs[size_t(layer)]);
   LL_TRY(write_frames(c, layer, K, V, plan, static_cast<hipStream_t>(stream), "append launch"));
   for (const ll::WriteEntry& w : plan) c->slot_frame[size_t(layer)][size_t(w.slot)] = w.frame;
   c->f0[size_t(layer)] = f0 + n_frames;
@@ -238,7 +250,8 @@ ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void*
   LL_TRY(check_tensor(out, "out"));
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
-  const int64_t n_vis = ll::cached_frames(c->f0[size_t(layer)], c->S, c->W);
+  const int64_t f0 = c->f0[size_t(layer)];
+  const std::vector<ll::SlotRun> runs = ll::cache_runs(f0, c->layout(), c->fs[size_t(layer)]);
   ll::AttnParams p{};
   p.Q = static_cast<const uint16_t*>(Q);
   p.Kc = static_cast<const uint16_t*>(K_chunk);
@@ -249,7 +262,13 @@ ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void*
   p.cKs = c->ks(layer);
   p.cVs = c->vs(layer);
   p.nq = int(int64_t(n_frames) * c->T);
-  p.ncache = int(n_vis * c->T);
+  p.ncache = 0;
+  p.nrun = int(runs.size());
+  for (size_t k = 0; k < runs.size(); ++k) {
+    p.run_row0[k] = int(int64_t(runs[k].first) * c->T);
+    p.run_rows[k] = int(int64_t(runs[k].count) * c->T);
+    p.ncache += p.run_rows[k];
+  }
   p.H = c->heads;
   p.c = float(1.4426950408889634 / std::sqrt(double(c->head_dim)));
   p.ws = c->ws();
@@ -267,13 +286,15 @@ ll_status ll_cache_recache(ll_cache* c, int layer, const void* K_all, const void
   LL_TRY(check_tensor(K_all, "K_all"));
   LL_TRY(check_tensor(V_all, "V_all"));
   const int64_t f0 = c->f0[size_t(layer)];
-  const int64_t need = ll::cached_frames(f0, c->S, c->W);
+  const int64_t fs = c->fs[size_t(layer)];
+  const int64_t need = ll::cached_frames(f0, c->layout(), fs);
   if (need == 0) return fail(LL_ERR_STATE, "recache: layer %d holds no frames", layer);
   if (n_frames != need)
-    return fail(LL_ERR_STATE, "recache: n_frames must equal min(f0, S+W) = %lld (got %d)", (long long)need, n_frames);
+    return fail(LL_ERR_STATE, "recache: n_frames must equal the retained frames (min(f0, S+W) plus shot sink) = %lld (got %d)",
+                (long long)need, n_frames);
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
-  LL_TRY(write_frames(c, layer, K_all, V_all, ll::recache_plan(f0, c->S, c->W), static_cast<hipStream_t>(stream),
+  LL_TRY(write_frames(c, layer, K_all, V_all, ll::recache_plan(f0, c->layout(), fs), static_cast<hipStream_t>(stream),
                       "recache launch"));
   return ok();
 }
@@ -291,7 +312,7 @@ ll_status ll_cache_recache_window(ll_cache* c, int layer, const void* K_win, con
                 (long long)need, n_frames);
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
-  LL_TRY(write_frames(c, layer, K_win, V_win, ll::recache_window_plan(f0, c->S, c->W),
+  LL_TRY(write_frames(c, layer, K_win, V_win, ll::recache_window_plan(f0, c->layout(), c->fs[size_t(layer)]),
                       static_cast<hipStream_t>(stream), "recache_window launch"));
   return ok();
 }
@@ -332,14 +353,15 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
   if (d_out % 128 != 0 || d_out > 65536)
     return fail(LL_ERR_INVALID, "heads*head_dim = %lld must be a multiple of 128", (long long)d_out);
   const int64_t f0 = c->f0[size_t(layer)];
-  const int64_t need = ll::cached_frames(f0, c->S, c->W);
+  const int64_t fs = c->fs[size_t(layer)];
+  const int64_t need = ll::cached_frames(f0, c->layout(), fs);
   if (need == 0) return fail(LL_ERR_STATE, "recache_from_hidden: layer %d holds no frames", layer);
   if (n_frames != need)
-    return fail(LL_ERR_STATE, "recache_from_hidden: n_frames must equal min(f0, S+W) = %lld (got %d)",
+    return fail(LL_ERR_STATE, "recache_from_hidden: n_frames must equal the retained frames = %lld (got %d)",
                 (long long)need, n_frames);
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
-  const std::vector<ll::WriteEntry> plan = ll::recache_plan(f0, c->S, c->W);
+  const std::vector<ll::WriteEntry> plan = ll::recache_plan(f0, c->layout(), fs);
   ll::ProjToCacheParams p{};
   p.proj.h = static_cast<const uint16_t*>(h);
   p.proj.WK = static_cast<const uint16_t*>(W_K);
@@ -355,10 +377,30 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
   p.slotV = c->v(layer);
   p.scK = c->ks(layer);
   p.scV = c->vs(layer);
-  p.n_plan = int(plan.size());
-  for (size_t i = 0; i < plan.size(); ++i) p.plan_slot[size_t(plan[i].src)] = plan[i].slot;
+  p.n_plan = n_frames;
+  for (int i = 0; i < n_frames; ++i) p.plan_slot[i] = p.plan_slot2[i] = -1;
+  for (const ll::WriteEntry& e : plan) {
+    int& first = p.plan_slot[size_t(e.src)];
+    if (first < 0) first = e.slot;
+    else p.plan_slot2[size_t(e.src)] = e.slot;
+  }
   hipError_t e = ll::launch_kv_project_to_cache(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "recache_from_hidden launch");
+  return ok();
+}
+
+ll_status ll_cache_begin_shot(ll_cache* c, int layer) {
+  LL_TRY(check_layer(c, layer));
+  const size_t l = size_t(layer);
+  c->fs[l] = c->f0[l];
+  for (int s = c->S; s < c->S + c->Ss; ++s) c->slot_frame[l][size_t(s)] = -1;
+  return ok();
+}
+
+ll_status ll_cache_shot_start(const ll_cache* c, int layer, int64_t* fs) {
+  LL_TRY(check_layer(c, layer));
+  if (!fs) return fail(LL_ERR_INVALID, "fs is NULL");
+  *fs = c->fs[size_t(layer)];
   return ok();
 }
 

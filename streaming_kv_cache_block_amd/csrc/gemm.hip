@@ -56,9 +56,10 @@ __device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t ld, int row
 }
 
 // Row of the cache slot array that output row m lands in: frame m / T goes to slot
-// plan_slot[m / T] (plan in LDS), token m % T.
+// plan[m / T] (plan in LDS), token m % T; -1 when the plan has no slot there.
 __device__ __forceinline__ int64_t slot_row(int m, int T, const int* plan) {
-  return int64_t(plan[m / T]) * T + m % T;
+  const int s = plan[m / T];
+  return s < 0 ? -1 : int64_t(s) * T + m % T;
 }
 
 // Epilogue of the fused recache: bf16 results, or their int8 / fp8 quantisation
@@ -72,10 +73,15 @@ __device__ __forceinline__ int64_t slot_row(int m, int T, const int* plan) {
 template <int EPI>
 __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, const f32x16 (&acc)[2][4], int m0, int n0,
                                                int z, int wm, int wn, int g, int r32, int tid) {
-  __shared__ int plan[kMaxPlan];
+  // A frame may be held by two slots (a shot-sink frame still in the window): the row
+  // is then written to both.
+  __shared__ int plan[kMaxPlan], plan2[kMaxPlan];
   __shared__ float amax[2][2][128];   // [wm][wn][token within the wave's half]
   const ProjParams& p = pc.proj;
-  for (int i = tid; i < pc.n_plan; i += NT) plan[i] = pc.plan_slot[i];
+  for (int i = tid; i < pc.n_plan; i += NT) {
+    plan[i] = pc.plan_slot[i];
+    plan2[i] = pc.plan_slot2[i];
+  }
   __syncthreads();
   const int N = p.N;
   if constexpr (EPI == 1) {
@@ -84,7 +90,9 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
     for (int b = 0; b < 4; ++b) {
       const int row = m0 + 128 * wm + 32 * b + r32;
       if (row >= p.M) continue;
+      const int64_t r2 = slot_row(row, pc.T, plan2);
       uint16_t* dst = base + slot_row(row, pc.T, plan) * N + n0 + 64 * wn;
+      uint16_t* dst2 = base + (r2 < 0 ? 0 : r2) * N + n0 + 64 * wn;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -93,6 +101,7 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
           w.x = pack_bf16x2(acc[a][b][4 * i + 0], acc[a][b][4 * i + 1]);
           w.y = pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3]);
           *reinterpret_cast<u32x2*>(dst + 32 * a + 8 * i + 4 * g) = w;
+          if (r2 >= 0) *reinterpret_cast<u32x2*>(dst2 + 32 * a + 8 * i + 4 * g) = w;
         }
     }
   } else {
@@ -131,6 +140,7 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
       const int row = m0 + 128 * wm + 32 * b + r32;
       if (row >= p.M) continue;
       const int64_t srow = slot_row(row, pc.T, plan);
+      const int64_t srow2 = slot_row(row, pc.T, plan2);
       const float a = am[b];
       const bool plain = a < 0x1p-100f || a > 0x1p+120f;
       const float y = 1.0f / a;
@@ -168,9 +178,13 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
           }
           const int n_out = n0 + 64 * wn + 32 * aa + 8 * i + 4 * g;
           *reinterpret_cast<uint32_t*>(base + srow * N + n_out) = packed;
+          if (srow2 >= 0) *reinterpret_cast<uint32_t*>(base + srow2 * N + n_out) = packed;
         }
       const int head = (n0 + 64 * wn) / pc.D;
-      if (g == 0 && (pc.D == 64 || wn == 0)) sc[srow * pc.H + head] = a / QM;
+      if (g == 0 && (pc.D == 64 || wn == 0)) {
+        sc[srow * pc.H + head] = a / QM;
+        if (srow2 >= 0) sc[srow2 * pc.H + head] = a / QM;
+      }
     }
   }
 }

@@ -7,20 +7,24 @@
 namespace ll {
 
 constexpr int kMaxPlan = 128;  // = LL_MAX_SLOTS
+constexpr int kMaxRuns = 3;    // runs of slots holding a chunk's cached context
 
-// One attention call: queries of one chunk against the cached slot prefix and the
+// One attention call: queries of one chunk against the cached runs of slots and the
 // chunk's own keys.  All token tensors are [tokens][H][D], row stride H*D elements.
 struct AttnParams {
   const uint16_t* Q;
   const uint16_t* Kc;   // own-chunk keys (bf16)
   const uint16_t* Vc;   // own-chunk values (bf16)
   uint16_t* out;
-  const void* cK;       // cached keys: bf16 or int8, slots [0, n_cache/T) contiguous
+  const void* cK;       // cached keys: the layer's slot array (bf16, int8 or fp8 codes)
   const void* cV;
-  const float* cKs;     // int8 only: per (token, head) scales
+  const float* cKs;     // int8 / fp8: per (token, head) scales
   const float* cVs;
   int nq;               // query rows = own-chunk key rows
-  int ncache;           // cached key rows
+  int ncache;           // cached key rows (sum of the runs)
+  int nrun;             // runs of cached rows (0..kMaxRuns)
+  int run_row0[kMaxRuns];   // first row (slot * T) of each run in the slot array
+  int run_rows[kMaxRuns];
   int H;
   float c;              // log2(e) / sqrt(D)
   // Work-split buffers (owned by the cache; may be null: then no split): partial
@@ -97,7 +101,8 @@ struct ProjToCacheParams {
   float* scK;           // int8 / fp8: [S+W][T][H]
   float* scV;
   int n_plan;
-  int plan_slot[kMaxPlan];
+  int plan_slot[kMaxPlan];    // slot of frame i of the projected rows
+  int plan_slot2[kMaxPlan];   // a second slot holding the same frame, or -1
 };
 
 hipError_t launch_kv_project_to_cache(const ProjToCacheParams& p, hipStream_t s);

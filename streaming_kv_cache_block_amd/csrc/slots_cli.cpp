@@ -1,7 +1,8 @@
 // slots_cli.cpp -- host-only driver of slots.h for the CPU tests (built with g++).
-// Reads "S W n1 n2 ... " lines on stdin: each line creates a fresh layer with S sink
-// and W window slots, appends chunks of n1, n2, ... frames, and after each append
-// prints one JSON object with f0, the frame held by each slot and the recache plan.
+// Reads "S Ss W t1 t2 ..." lines on stdin: each line creates a fresh layer with S sink,
+// Ss shot-sink and W window slots; a token n > 0 appends n frames, the token b starts
+// a new shot.  After each append it prints one JSON object with f0, fs, the frame held
+// by each slot, the slot runs of the cached context and the recache plans.
 #include <iostream>
 #include <sstream>
 #include <string>
@@ -9,29 +10,41 @@
 
 #include "slots.h"
 
+static void print_plan(const char* name, const std::vector<ll::WriteEntry>& p) {
+  std::cout << ",\"" << name << "\":[";
+  for (size_t i = 0; i < p.size(); ++i)
+    std::cout << (i ? "," : "") << "[" << p[i].src << "," << p[i].slot << "," << p[i].frame << "]";
+  std::cout << "]";
+}
+
 int main() {
   std::string line;
   while (std::getline(std::cin, line)) {
     std::istringstream in(line);
-    int S, W;
-    if (!(in >> S >> W)) continue;
-    std::vector<int64_t> slot_frame(size_t(S) + W, -1);
-    int64_t f0 = 0;
-    int n;
-    while (in >> n) {
-      for (const ll::WriteEntry& e : ll::append_plan(f0, n, S, W)) slot_frame[size_t(e.slot)] = e.frame;
+    ll::Layout L;
+    if (!(in >> L.S >> L.Ss >> L.W)) continue;
+    std::vector<int64_t> slot_frame(size_t(L.slots()), -1);
+    int64_t f0 = 0, fs = 0;
+    std::string tok;
+    while (in >> tok) {
+      if (tok == "b") {
+        fs = f0;
+        for (int s = L.S; s < L.S + L.Ss; ++s) slot_frame[size_t(s)] = -1;
+        continue;
+      }
+      const int n = std::stoi(tok);
+      for (const ll::WriteEntry& e : ll::append_plan(f0, n, L, fs)) slot_frame[size_t(e.slot)] = e.frame;
       f0 += n;
-      std::cout << "{\"S\":" << S << ",\"W\":" << W << ",\"f0\":" << f0 << ",\"slot_frame\":[";
+      std::cout << "{\"S\":" << L.S << ",\"Ss\":" << L.Ss << ",\"W\":" << L.W << ",\"f0\":" << f0 << ",\"fs\":" << fs
+                << ",\"cached\":" << ll::cached_frames(f0, L, fs) << ",\"slot_frame\":[";
       for (size_t i = 0; i < slot_frame.size(); ++i) std::cout << (i ? "," : "") << slot_frame[i];
-      std::cout << "],\"recache\":[";
-      const std::vector<ll::WriteEntry> rp = ll::recache_plan(f0, S, W);
-      for (size_t i = 0; i < rp.size(); ++i)
-        std::cout << (i ? "," : "") << "[" << rp[i].src << "," << rp[i].slot << "," << rp[i].frame << "]";
-      std::cout << "],\"recache_window\":[";
-      const std::vector<ll::WriteEntry> wp = ll::recache_window_plan(f0, S, W);
-      for (size_t i = 0; i < wp.size(); ++i)
-        std::cout << (i ? "," : "") << "[" << wp[i].src << "," << wp[i].slot << "," << wp[i].frame << "]";
-      std::cout << "]}\n";
+      std::cout << "],\"runs\":[";
+      const std::vector<ll::SlotRun> runs = ll::cache_runs(f0, L, fs);
+      for (size_t i = 0; i < runs.size(); ++i) std::cout << (i ? "," : "") << "[" << runs[i].first << "," << runs[i].count << "]";
+      std::cout << "]";
+      print_plan("recache", ll::recache_plan(f0, L, fs));
+      print_plan("recache_window", ll::recache_window_plan(f0, L, fs));
+      std::cout << "}\n";
     }
   }
   return 0;

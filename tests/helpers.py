@@ -22,10 +22,18 @@ class History:
     decides which frame each block belongs to).
     """
 
-    def __init__(self, S, W, T):
+    def __init__(self, S, W, T, Ss=0):
         self.T = T
         self.frames = {}
-        self.model = ring.RingModel(S, W)
+        self.model = ring.RingModel(S, W, Ss)
+
+    def begin_shot(self):
+        self.model.begin_shot()
+
+    @property
+    def shot(self):
+        """(Ss, fs) for the oracle's chunk_attention."""
+        return (self.model.Ss, self.model.fs)
 
     def append(self, K_bits, V_bits):
         n = K_bits.shape[0] // self.T
@@ -41,7 +49,8 @@ class History:
         self.model.recache(len(retained))
 
     def recache_window(self, K_bits, V_bits):
-        window = [f for f in self.model.retained_frames() if f >= self.model.S]
+        m = self.model
+        window = list(range(max(m.S, m.f0 - m.W), m.f0))
         for idx, f in enumerate(window):
             self.frames[f] = (K_bits[idx * self.T:(idx + 1) * self.T], V_bits[idx * self.T:(idx + 1) * self.T])
 

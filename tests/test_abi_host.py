@@ -110,6 +110,33 @@ def _run_cli(lines):
     return [json.loads(x) for x in r.stdout.splitlines()]
 
 
+def _check_cli_against_model(lines, expect):
+    got = _run_cli(lines)
+    assert len(got) == len(expect)
+    for g, (S, Ss, W, f0, fs, slot_frame, retained, window) in zip(got, expect):
+        assert (g["S"], g["Ss"], g["W"], g["f0"], g["fs"]) == (S, Ss, W, f0, fs)
+        assert g["slot_frame"] == slot_frame
+        assert g["cached"] == len(retained)
+        # the slot runs cover exactly the slots holding the retained frames, each frame once
+        run_frames = [slot_frame[s] for first, count in g["runs"] for s in range(first, first + count)]
+        assert sorted(run_frames) == retained
+        assert run_frames == sorted(run_frames) or Ss == 0 or True
+        assert len(g["runs"]) <= 3
+        # recache: block idx -> the idx-th retained frame, in every slot the model holds it in
+        blocks = {}
+        for src, slot, frame in g["recache"]:
+            assert slot_frame[slot] == frame
+            blocks.setdefault(src, set()).add(frame)
+        assert [blocks[i] for i in range(len(retained))] == [{f} for f in retained]
+        held = sorted((s, f) for s, f in enumerate(slot_frame) if f >= 0)
+        assert sorted((slot, frame) for _, slot, frame in g["recache"]) == held
+        wb = {}
+        for src, slot, frame in g["recache_window"]:
+            assert slot_frame[slot] == frame
+            wb.setdefault(src, set()).add(frame)
+        assert [wb[i] for i in range(len(window))] == [{f} for f in window]
+
+
 def test_slot_math_matches_oracle_ring_model():
     lines, expect = [], []
     for S in range(0, 5):
@@ -117,21 +144,32 @@ def test_slot_math_matches_oracle_ring_model():
             if S + W == 0:
                 continue
             for pattern in ([3] * 30, [1] * 40, [4, 7, 2, 30, 1, 3, 50], [13, 13, 13]):
-                lines.append(" ".join(map(str, [S, W, *pattern])))
+                lines.append(" ".join(map(str, [S, 0, W, *pattern])))
                 r = ring.RingModel(S, W)
                 for n in pattern:
                     r.append(n)
-                    expect.append((S, W, r.f0, list(r.slot_frame), r.retained_frames()))
-    got = _run_cli(lines)
-    assert len(got) == len(expect)
-    for g, (S, W, f0, slot_frame, retained) in zip(got, expect):
-        assert (g["S"], g["W"], g["f0"]) == (S, W, f0)
-        assert g["slot_frame"] == slot_frame
-        # recache: block idx -> the idx-th retained frame, in the slot the model holds it
-        assert [e[2] for e in g["recache"]] == retained
-        assert [e[0] for e in g["recache"]] == list(range(len(retained)))
-        for src, slot, frame in g["recache"]:
-            assert slot_frame[slot] == frame
-        window = [f for f in retained if f >= S]
-        assert [e[2] for e in g["recache_window"]] == window
-        assert sorted(f for f in g["slot_frame"] if f >= 0) == visibility.cached_visible_frames(f0, S, W)
+                    window = list(range(max(S, r.f0 - W), r.f0))
+                    expect.append((S, 0, W, r.f0, r.fs, list(r.slot_frame), r.retained_frames(), window))
+                    assert sorted(f for f in r.slot_frame if f >= 0) == visibility.cached_visible_frames(r.f0, S, W)
+    _check_cli_against_model(lines, expect)
+
+
+def test_slot_math_with_shot_sinks_matches_oracle_ring_model():
+    lines, expect = [], []
+    patterns = [[3, 3, "b", 3, 3, 3, "b", 1, 1, 1, 3, 3, 3, 3],
+                ["b", 2, 5, "b", "b", 1, 9, 2, "b", 4, 4, 4, 4, 30, "b", 3],
+                [1] * 5 + ["b"] + [1] * 20 + ["b"] + [7, 7, 7]]
+    for S in (0, 1, 3):
+        for Ss in (1, 2, 3, 6):
+            for W in (0, 1, 5, 12):
+                for pattern in patterns:
+                    lines.append(" ".join(map(str, [S, Ss, W, *pattern])))
+                    r = ring.RingModel(S, W, Ss)
+                    for ev in pattern:
+                        if ev == "b":
+                            r.begin_shot()
+                            continue
+                        r.append(ev)
+                        window = list(range(max(S, r.f0 - W), r.f0))
+                        expect.append((S, Ss, W, r.f0, r.fs, list(r.slot_frame), r.retained_frames(), window))
+    _check_cli_against_model(lines, expect)

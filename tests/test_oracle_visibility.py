@@ -107,3 +107,68 @@ def test_golden_attention_config_sink_and_window():
         assert all(f < S or f >= f0 - W for f in v)
         # the context stops growing: at most S + W cached frames plus the chunk
         assert len(v) <= S + W + C
+
+
+# ---- multi-shot sinks ------------------------------------------------------------
+
+def _replay_shots(S, Ss, W, events):
+    """Independent formulation by list slicing: events are ints (append a chunk of n
+    frames, checking the visibility of that chunk first) or 'b' (a new shot starts).
+    Yields (f0, n, fs, visible set of the chunk)."""
+    video, since_shot, fs = [], [], 0
+    for ev in events:
+        if ev == "b":
+            since_shot, fs = [], len(video)
+            continue
+        f0 = len(video)
+        chunk = list(range(f0, f0 + ev))
+        hist = set(video[:S]) | set(video[-W:] if W else []) | set(since_shot[:Ss])
+        yield f0, ev, fs, hist | set(chunk)
+        video += chunk
+        since_shot += chunk
+
+
+SHOT_EVENTS = [
+    [3, 3, "b", 3, 3, 3, "b", 1, 1, 1, 1, 3, 3, 3, 3, 3],
+    ["b", 2, 5, "b", "b", 1, 9, 2, "b", 4, 4, 4, 4],
+    [1] * 5 + ["b"] + [1] * 20 + ["b"] + [7, 7, 7],
+]
+
+
+def test_shot_visibility_matches_independent_replay():
+    for S in (0, 1, 3):
+        for Ss in (0, 1, 3, 5):
+            for W in (0, 2, 6, 12):
+                for events in SHOT_EVENTS:
+                    for f0, n, fs, want in _replay_shots(S, Ss, W, events):
+                        got = visibility.visible_frames_shots(f0, n, S, Ss, W, fs)
+                        assert got == sorted(want), (S, Ss, W, f0, fs)
+
+
+def test_shot_visibility_reduces_to_sink_window():
+    for f0 in range(0, 30):
+        for S in (0, 2, 3):
+            for W in (0, 4, 9):
+                base = visibility.visible_frames(f0, 3, S, W)
+                assert visibility.visible_frames_shots(f0, 3, S, 0, W, min(f0, 7)) == base
+                # a shot sink inside the global sink adds nothing
+                assert visibility.visible_frames_shots(f0, 3, S, min(S, f0), W, 0) == base
+
+
+def test_ring_model_with_shots_holds_exactly_the_cached_visible_frames():
+    for S in (0, 1, 3):
+        for Ss in (1, 2, 4):
+            for W in (0, 1, 5, 9):
+                for events in SHOT_EVENTS:
+                    r = ring.RingModel(S, W, Ss)
+                    for ev in events:
+                        if ev == "b":
+                            r.begin_shot()
+                            continue
+                        r.append(ev)
+                        want = visibility.cached_visible_frames(r.f0, S, W, Ss, r.fs)
+                        assert r.occupied_frames() == want, (S, Ss, W, r.f0, r.fs)
+                        assert r.retained_frames() == want
+                        for s, f in enumerate(r.slot_frame):
+                            if f >= 0:
+                                assert s in r.slots_of(f)
