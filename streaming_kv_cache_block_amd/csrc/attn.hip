@@ -180,16 +180,58 @@ struct QTile {
   }
 };
 
-// Order of the key tiles.  The keys are the cached runs (up to kMaxRuns runs of rows of
-// the slot array) and the own chunk; each is tiled on its own, so only the last tile of
+// Order of the key tiles of a launch whose cached context is one run of rows (every
+// cache without a shot sink): the (at most two) partial tiles -- the last tile of the
+// run and of the own chunk -- come first, so that the long stretch of full tiles after
+// them carries no masking code; then the full cache tiles, then the full own-chunk
+// tiles.  Softmax attention does not depend on the order of its keys.
+struct TileOrder1 {
+  int n1, n2, np1, np2, ncache, nq, r0;
+  __device__ explicit TileOrder1(const AttnParams& p)
+      : ncache(p.nrun ? p.run_rows[0] : 0), nq(p.nq), r0(p.nrun ? p.run_row0[0] : 0) {
+    n1 = (ncache + BN - 1) / BN;
+    n2 = (nq + BN - 1) / BN;
+    np1 = (ncache % BN) != 0;
+    np2 = (nq % BN) != 0;
+  }
+  __device__ int npart() const { return np1 + np2; }
+  __device__ int full1_end() const { return np1 + np2 + n1 - np1; }   // end of the full cache tiles
+  __device__ int total() const { return n1 + n2; }
+  __device__ TileInfo at(int j) const {
+    TileInfo t;
+    if (j < np1 + np2) {
+      if (j == 0 && np1) {
+        t.seg = 0;
+        t.start = r0 + (n1 - 1) * BN;
+        t.cnt = ncache - (n1 - 1) * BN;
+      } else {
+        t.seg = 1;
+        t.start = (n2 - 1) * BN;
+        t.cnt = nq - t.start;
+      }
+    } else if (j < full1_end()) {
+      t.seg = 0;
+      t.start = r0 + (j - np1 - np2) * BN;
+      t.cnt = BN;
+    } else {
+      t.seg = 1;
+      t.start = (j - full1_end()) * BN;
+      t.cnt = BN;
+    }
+    return t;
+  }
+};
+
+// General order of the key tiles (a shot sink can split the cached context).  The keys
+// are the cached runs (up to kMaxRuns runs of rows of the slot array) and the own chunk; each is tiled on its own, so only the last tile of
 // each may be partial.  The partial tiles come first, so that the long stretch of full
 // tiles after them carries no masking code; then the full cache tiles run by run, then
 // the full own-chunk tiles.  Softmax attention does not depend on the order of its keys.
 // (All loops are unrolled over the run count so the tables stay in scalar registers.)
-struct TileOrder {
+struct TileOrderN {
   int r0[kMaxRuns], rn[kMaxRuns], fc[kMaxRuns];   // first row, rows, full tiles per run
   int nq, np, nfc, pmask;   // own rows, partial tiles, full cache tiles, runs with a partial tile
-  __device__ explicit TileOrder(const AttnParams& p) : nq(p.nq), np(0), nfc(0), pmask(0) {
+  __device__ explicit TileOrderN(const AttnParams& p) : nq(p.nq), np(0), nfc(0), pmask(0) {
 #pragma unroll
     for (int k = 0; k < kMaxRuns; ++k) {
       r0[k] = k < p.nrun ? p.run_row0[k] : 0;
@@ -536,7 +578,7 @@ struct XcdPlan {
   __host__ __device__ int n_tail(int b) const { return ((b + 1) * t - 1) / L - b * t / L + 1; }
 };
 
-template <int D, int NQB, int NW, int MINB, int KVQ>
+template <int D, int NQB, int NW, int MINB, int KVQ, bool RUNS>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p, const Split sp) {
   using G = Geo<D, NW>;
   // Two buffers per operand as separate LDS objects: the buffer parity is a compile-time
@@ -563,7 +605,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   Attn<D, NQB, NW, KV8> A;
   A.init_offsets(lane);
 
-  const TileOrder order(p);
+  // RUNS: the cached context may be several runs of slots (shot sink)
+  const std::conditional_t<RUNS, TileOrderN, TileOrder1> order(p);
   const int ntiles = order.total();
   uint32_t loff[Geo<D, NW>::DMA_PER_WAVE];
 #pragma unroll
@@ -752,7 +795,10 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   }
   sp.on = on;
   const int grid = on ? p.n_cu : (sp.B + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KVQ>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
+  if (p.nrun > 1)
+    hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KVQ, true>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KVQ, false>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
   return hipGetLastError();
 }
 
