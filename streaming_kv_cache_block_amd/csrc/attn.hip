@@ -504,32 +504,47 @@ struct Attn {
   // Combine this wave's own piece (registers) with the partial results of the other
   // pieces of the block over disjoint key sets:
   //   M = max_i m_i,  O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,
-  // then store.  The same identity as the running rescale inside one piece.
-  __device__ __forceinline__ void merge_store(const float* o0, const float* o1, int n_others, int rows, int wave,
-                                              uint16_t* out, int q0, int nq, int64_t rs, int h) {
+  // then store.  The same identity as the running rescale inside one piece.  The sums
+  // run over the pieces in block order (head piece, then the tail pieces) whichever
+  // piece does the merge, so the result does not depend on which one arrived last.
+  //   slot_k: partial of piece k (unused for k == own); n: pieces (2 or 3)
+  __device__ __forceinline__ void merge_store(const float* s0, const float* s1, const float* s2, int own, int n,
+                                              int rows, int wave, uint16_t* out, int q0, int nq, int64_t rs,
+                                              int h) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int row = wave * 32 * NQB + 32 * qb + r32;
-      float M = m[qb];
-      for (int k = 0; k < n_others; ++k) M = fmaxf(M, coherent_load((k ? o1 : o0) + rows * D + row));
-      const float fo = fast_exp2(m[qb] - M);
-      float L = (l[qb] + __shfl_xor(l[qb], 32)) * fo;
+      const float lown = l[qb] + __shfl_xor(l[qb], 32);
+      float mk[3], lk[3];
 #pragma unroll
-      for (int e = 0; e < D / 32; ++e) O[qb][e] *= fo;
-      for (int k = 0; k < n_others; ++k) {
-        const float* sl = k ? o1 : o0;
-        const float f = fast_exp2(coherent_load(sl + rows * D + row) - M);
-        L += f * coherent_load(sl + rows * D + rows + row);
-        const __amdgpu_buffer_rsrc_t rsrc = coherent_rsrc(sl);
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 v = coherent_load4(rsrc, 4u * uint32_t(row * D + 32 * e + 8 * i + 4 * g));
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) O[qb][e][4 * i + jj] += f * v[jj];
-          }
+      for (int k = 0; k < 3; ++k) {
+        const float* sl = k == 0 ? s0 : k == 1 ? s1 : s2;
+        const bool mem = k < n && k != own;
+        mk[k] = k == own ? m[qb] : (mem ? coherent_load(sl + rows * D + row) : -__builtin_inff());
+        lk[k] = k == own ? lown : (mem ? coherent_load(sl + rows * D + rows + row) : 0.0f);
       }
+      const float M = fmaxf(fmaxf(mk[0], mk[1]), mk[2]);
+      float f[3];
+      float L = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        f[k] = k < n ? fast_exp2(mk[k] - M) : 0.0f;
+        if (k < n) L += f[k] * lk[k];
+      }
+      const __amdgpu_buffer_rsrc_t r0 = coherent_rsrc(s0), r1 = coherent_rsrc(s1), r2 = coherent_rsrc(s2);
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t off = 4u * uint32_t(row * D + 32 * e + 8 * i + 4 * g);
+          const f32x4 mine = f32x4{O[qb][e][4 * i], O[qb][e][4 * i + 1], O[qb][e][4 * i + 2], O[qb][e][4 * i + 3]};
+          const f32x4 x0 = own == 0 ? mine : coherent_load4(r0, off);
+          const f32x4 x1 = own == 1 ? mine : coherent_load4(r1, off);
+          f32x4 acc = x0 * f[0] + x1 * f[1];
+          if (n > 2) acc = acc + (own == 2 ? mine : coherent_load4(r2, off)) * f[2];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) O[qb][e][4 * i + jj] = acc[jj];
+        }
       // store() halves the row sum across the lane pair: hand it half of L per lane
       l[qb] = 0.5f * L;
     }
@@ -723,11 +738,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
       __syncthreads();
     }
     if (sm_last) {
-      // the block's slots: blk (head piece), B + 2 blk + k (tail pieces k < npc - 1)
-      const int s0 = blk == slot ? sp.B + 2 * blk : blk;
-      const int s1 = sp.B + 2 * blk + ((blk == slot || sp.B + 2 * blk == slot) ? 1 : 0);
-      A.merge_store(sp.ws + s0 * slot_floats, sp.ws + s1 * slot_floats, npc - 1, ROWS, wave, p.out, q0, p.nq,
-                    rs, h);
+      // the block's pieces in order: blk (head piece), B + 2 blk + k (tail pieces)
+      const int own = slot == blk ? 0 : slot - (sp.B + 2 * blk) + 1;
+      A.merge_store(sp.ws + int64_t(blk) * slot_floats, sp.ws + int64_t(sp.B + 2 * blk) * slot_floats,
+                    sp.ws + int64_t(sp.B + 2 * blk + 1) * slot_floats, own, npc, ROWS, wave, p.out, q0, p.nq, rs,
+                    h);
       if (tid == 0) coherent_store(sp.cnt + blk, 0);   // ready for the next call on the stream
     }
     __syncthreads();

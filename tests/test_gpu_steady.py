@@ -170,3 +170,39 @@ def test_frame_id_probe_at_full_shape(torch_gpu):
             assert np.abs(got - want[None, None, :]).max() <= np.abs(want).max() * 2 ** -7, (k, f0)
         cache.append(0, kz, v)
         f0 += C
+
+
+@pytest.mark.parametrize("H,C,D,kv", [
+    (8, 3, 128, "bf16"),    # 152 blocks: per-XCD split, 19 blocks per XCD
+    (8, 4, 128, "bf16"),    # 200 blocks
+    (12, 2, 128, "int8"),   # 156 blocks, quantised cache tiles in the split walk
+    (16, 2, 128, "bf16"),   # 208 blocks
+    (24, 1, 128, "fp8"),    # 168 blocks, one-frame chunk
+    (12, 3, 64, "bf16"),    # 228 blocks of the head_dim-64 kernel (two query blocks per wave)
+    (12, 4, 128, "bf16"),   # 300 blocks: more blocks than CUs, one workgroup per block
+])
+def test_attention_split_walk_shapes(torch_gpu, H, C, D, kv):
+    """Block counts below the CU count take the per-XCD split walk (heads walk the first
+    J - t key tiles, spare workgroups the tails, partials merged); sampled rows of every
+    query tile against the oracle, including the first and last rows of each tile."""
+    T, S, W = 1560, 3, 12
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
+    hist = History(S, W, T)
+    kb = synth.normal_bf16((16 * T, H, D), 0.5, 900, H, C, D, 0)
+    vb = synth.normal_bf16((16 * T, H, D), 0.5, 900, H, C, D, 1)
+    cache.append(0, synth.to_device(kb), synth.to_device(vb))
+    hist.append(kb, vb)
+    nq = C * T
+    q, kc, vc = (synth.normal_bf16((nq, H, D), 0.5, 901, H, C, D, t) for t in range(3))
+    out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+    tile_rows = 256
+    rows = set(sample_rows(nq, T, seed=H * 10 + C, n_random=24))
+    for t0 in range(0, nq, tile_rows):
+        rows |= {t0, min(t0 + tile_rows, nq) - 1}
+    rows = sorted(rows)
+    ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv=kv, rows=rows)
+    mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"H={H} C={C} D={D} kv={kv}")
+    _log(f"split walk H={H} C={C} D={D} kv={kv}: {len(rows)} rows, max-abs {mx:.2e} mean-abs {mn:.2e}")
+    # the same chunk again: the arrival counters were reset by the merges
+    out2 = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+    assert np.array_equal(synth.to_bits(out2), synth.to_bits(out))
