@@ -20,14 +20,18 @@
 //     widened to bf16 in registers on the way (exact for |q| <= 127).
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA: a
 //     lane then holds one query's scores for 16 keys of each 32-key block, so the
-//     running row max needs one exchange with lane ^ 32 and the row sum stays per
-//     lane until the end.  Each K fragment read from LDS feeds NQB MFMAs.
+//     running row max needs one register exchange with lane ^ 32
+//     (v_permlane32_swap) and the row sum stays per lane until the end.  Each K
+//     fragment read from LDS feeds NQB MFMAs.
 //   * The lane's probabilities are the B operand of O^T = V^T P^T as they are; the
 //     A operand V^T (8 keys of one d per lane, keys matched to the lane's B slots)
 //     comes from two transpose reads (ds_read_b64_tr_b16) of the natural V tile.
 //   * Online softmax in base 2, log2(e)/sqrt(D) folded into one FMA; the running
 //     max is only raised (and O, l rescaled) when a score exceeds it by more than
 //     2^8, which keeps every probability <= 256 and skips almost all rescales.
+//     Full bf16 tiles first take the probabilities against the running max as it
+//     stands and check the bound on the lane's tile sum; only tiles that fail it
+//     (rare after the first) compute the tile max, rescale and take them again.
 //   * int8 caches: the per-key K scale multiplies the score column and the V scale
 //     the probability column before rounding to bf16 (LongLive-2.0 explainer,
 //     wmrh.cn, §15.3: dequantisation fused into the consumer, not a separate pass).
@@ -49,6 +53,10 @@ constexpr float kLazyThreshold = 8.0f;   // log2 units
 #define LL_PIECE_TILES 12
 #endif
 constexpr int kPieceTiles = LL_PIECE_TILES;   // per-piece overhead of a split walk, in tiles
+#ifndef LL_SPEC
+#define LL_SPEC 1
+#endif
+constexpr bool kSpecSoftmax = LL_SPEC;   // full bf16 tiles: probabilities against the running max first
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -368,7 +376,10 @@ struct Attn {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[qb][b][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      {  // lanes l and l ^ 32 hold the two halves of a query's keys: exchange in registers
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+      }
       if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kLazyThreshold)) {
         const float mnew = fmaxf(m[qb], mx);
         const float alpha = fast_exp2(m[qb] - mnew);
@@ -445,15 +456,90 @@ struct Attn {
       }
   }
 
+  // Probabilities of a full unscaled tile against running max mq, packed to bf16 in
+  // the P*V operand layout; returns the lane's sum of the packed values (the weights
+  // P*V applies).
+  __device__ __forceinline__ float exp_pack(const f32x16 (&S)[2], float mq, bf16x8 (&P)[4]) const {
+    float part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = u >> 1, v0 = 8 * (u & 1);
+      float e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) e[t] = fast_exp2(__builtin_fmaf(S[b][v0 + t], c, -mq));
+      u32x4 w;
+      w.x = pack_bf16x2(e[0], e[1]);
+      w.y = pack_bf16x2(e[2], e[3]);
+      w.z = pack_bf16x2(e[4], e[5]);
+      w.w = pack_bf16x2(e[6], e[7]);
+      P[u] = as_bf16x8(w);
+      part[u] = dot2_ones(w.w, dot2_ones(w.z, dot2_ones(w.y, dot2_ones(w.x, 0.0f))));
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  }
+
+  // Full unscaled tile with the probabilities first taken against the running max as it
+  // stands.  They are non-negative, so all of a lane's probabilities are at most 2^8
+  // exactly when its tile sum is; then the tile needs no new max (the same bound the
+  // lazy rescale keeps).  Otherwise (a score more than 8 above the running max, or the
+  // first tile of a walk, where the max is -inf) the scores are recomputed from the K
+  // tile, still in LDS, the running max is raised to the tile's max and O and l are
+  // rescaled before the probabilities are taken again.  The common case skips the
+  // per-tile max and its exchange between the two lanes of a query.  (Scaled int8 /
+  // fp8 tiles keep softmax(): there the extra scale work ate the gain.)
+  __device__ __forceinline__ void tile_spec(const uint16_t* lk, const uint16_t* lv) {
+    constexpr float kBound = float(1 << int(kLazyThreshold));
+    f32x16 S[NQB][2];
+    bf16x8 P[NQB][4];
+    scores<false, false>(lk, nullptr, BN, false, S);
+    float rsum[NQB];
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      rsum[qb] = exp_pack(S[qb], m[qb], P[qb]);
+      over |= !(rsum[qb] <= kBound);
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      // an offset the compiler cannot see through: the K fragments are read again here
+      // instead of being held in registers across the exponentials for this rare case
+      int z = 0;
+      asm volatile("" : "+s"(z));
+      scores<false, false>(lk + z, nullptr, BN, false, S);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = S[qb][0][0];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[qb][b][v]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const float mnew = fmaxf(m[qb], fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
+        const float alpha = fast_exp2(m[qb] - mnew);
+        m[qb] = mnew;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) O[qb][e] *= alpha;
+        rsum[qb] = exp_pack(S[qb], mnew, P[qb]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l[qb] += rsum[qb];
+    pv(lv, P);
+  }
+
   // One whole tile from LDS: scores, softmax, P*V.
   template <bool MASK, bool SCALED>
   __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lks, const float* lvs,
                                        int cnt, bool scaled = SCALED) {
-    f32x16 S[NQB][2];
-    bf16x8 P[NQB][4];
-    scores<MASK, SCALED>(lk, lks, cnt, scaled, S);
-    softmax<SCALED>(S, lvs, scaled, P);
-    pv(lv, P);
+    if constexpr (kSpecSoftmax && !MASK && !SCALED) {
+      tile_spec(lk, lv);
+    } else {
+      f32x16 S[NQB][2];
+      bf16x8 P[NQB][4];
+      scores<MASK, SCALED>(lk, lks, cnt, scaled, S);
+      softmax<SCALED>(S, lvs, scaled, P);
+      pv(lv, P);
+    }
   }
 
   // Normalise and store O (lane: query r32, d = 32 e + 8 i + 4 g + [0, 4)).

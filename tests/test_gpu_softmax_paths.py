@@ -1,0 +1,100 @@
+"""GPU parity of the running-max paths of the attention walk.
+
+Full bf16 tiles take their probabilities against the running max first and redo the
+tile (new max, O and l rescaled) only when a lane's tile sum exceeds 2^8; the other
+tiles compute the tile max and rescale when it is more than 8 (log2 units) above the
+running max.  These inputs make both happen on purpose, away from the first tile:
+
+  * staircase scores: every query is e_0 (plus small noise), and K of token t of frame
+    f has K[0] such that its score is 12 f + 5 [t >= 64] in log2 units, so frame by
+    frame a tile's max lies far above the running max, and between the two 64-key
+    halves of a frame a tile's max is only 5 above it while its sum is 32 * 2^5 > 2^8;
+  * random scores with a large spread (Q, K, V ~ N(0, 3^2)).
+
+Head_dim 64 and 128; bf16, int8 and fp8 caches (the cache tiles of the low-bit caches
+take the scaled path, the chunk's own keys the bf16 one).  Every output is compared
+with the oracle in full.  The N(0, 3^2) inputs give nearly one-hot rows and outputs up
+to about 12 in magnitude, where one bf16 ulp is 2^-4; there each output must lie within
+2e-2 + 2^-6 |ref| of the oracle (the acceptance bound plus two bf16 half-ulps of the
+output, which also covers the bf16-rounded probabilities), mean-abs within 3 * 2e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import streaming_kv_cache_block_amd as ll
+import synth
+from oracle import attention, bf16
+from synth import configs
+
+from helpers import History, check_slots, compare_attention
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ll.lib()
+    return torch
+
+
+def _staircase(f0, n_frames, T, H, D, seed):
+    """bf16 bits (q, k, v) of frames f0 .. f0 + n_frames - 1 with the staircase scores."""
+    rng = np.random.default_rng(seed + 7919 * f0)
+    n = n_frames * T
+    q = rng.normal(0.0, 0.05, (n, H, D)).astype(np.float32)
+    q[:, :, 0] = 1.0
+    k = rng.normal(0.0, 0.05, (n, H, D)).astype(np.float32)
+    f = f0 + np.arange(n) // T
+    t = np.arange(n) % T
+    level = 12.0 * f + 5.0 * (t >= 64)
+    k[:, :, 0] = (level * math.sqrt(D) / math.log2(math.e))[:, None]
+    v = rng.normal(0.0, 1.0, (n, H, D)).astype(np.float32)
+    return tuple(synth.f32_to_bf16_bits(x) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_staircase_scores(torch_gpu, D, kv):
+    T, H, S, W, C = 128, 2, 1, 4, 2
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
+    hist = History(S, W, T)
+    for chunk in range(6):
+        f0 = hist.f0
+        print(f"staircase D={D} kv={kv} chunk {chunk} f0={f0}", flush=True)
+        q, kc, vc = _staircase(f0, C, T, H, D, seed=D)
+        out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+        ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv)
+        compare_attention(out, ref, f"staircase D={D} kv={kv} chunk {chunk}")
+        cache.append(0, synth.to_device(kc), synth.to_device(vc))
+        hist.append(kc, vc)
+    check_slots(cache, 0, hist, kv=kv)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_wide_score_spread(torch_gpu, D, kv):
+    T, H, S, W, C = 96, 2, 2, 5, 3
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
+    hist = History(S, W, T)
+    shape = (C * T, H, D)
+    for chunk in range(5):
+        f0 = hist.f0
+        print(f"spread D={D} kv={kv} chunk {chunk} f0={f0}", flush=True)
+        q, kc, vc = (synth.normal_bf16(shape, 3.0, 611, D, chunk, i) for i in range(3))
+        out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+        ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv)
+        got = bf16.to_f32(synth.to_bits(out)).astype(np.float64)
+        err = np.abs(got - ref)
+        bound = 2e-2 + 2.0 ** -6 * np.abs(ref)
+        worst = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert np.isfinite(got).all()
+        assert (err <= bound).all(), f"spread D={D} kv={kv} chunk {chunk}: err {err[worst]:.3g} at {worst}, ref {ref[worst]:.3g}"
+        assert err.mean() <= 6e-3, f"spread D={D} kv={kv} chunk {chunk}: mean-abs {err.mean():.3g}"
+        cache.append(0, synth.to_device(kc), synth.to_device(vc))
+        hist.append(kc, vc)
