@@ -3,9 +3,11 @@
 ll_cache_recache_from_hidden must leave exactly the bytes that ll_kv_project
 followed by ll_cache_recache leaves (bf16 slots, or int8 / fp8 codes and fp32 scales),
 and those bytes must match the oracle's cache model fed the projected K/V.
-Shapes: ragged token counts (T not a multiple of the 256-token tile), head_dim 64
-(two heads per 128-output tile) and 128, caches that are not yet full and caches
-whose ring has wrapped, and the full 12-head x 128 / 1560-token / 15-frame recache.
+Shapes: ragged token counts (T not a multiple of the 192- or 256-token tile), head_dim
+64 (two heads per 128-output tile) and 128, output counts that take the 256-wide tiles
+(a multiple of 256) and the 128-wide ones, a contraction of a single step, caches that
+are not yet full and caches whose ring has wrapped, and the full 12-head x 128 /
+1560-token / 15-frame recache.
 Inputs: bf16 N(0, 1) hidden states and N(0, 1/d_in) weights from fixed seeds.
 """
 
@@ -84,6 +86,9 @@ def _case(torch, H, D, T, S, W, d_in, kv, appends, seed):
     (3, 128, 40, 2, 5, 256, [1, 4, 3, 2]),     # 3 heads, wrapped
     (1, 128, 7, 0, 4, 64, [2, 3]),             # no sink, tiny frames
     (4, 64, 130, 3, 0, 320, [2, 2]),           # sink only
+    (2, 128, 17, 1, 3, 64, [2, 2]),            # 256 outputs (wide tiles), one 64-wide contraction step
+    (1, 128, 9, 2, 2, 64, [1, 3]),             # 128 outputs, two 32-wide contraction steps
+    (4, 128, 100, 2, 4, 128, [3, 3, 3]),       # 512 outputs (two wide output tiles), 600 tokens
 ])
 def test_fused_recache_matches_project_then_recache(torch_gpu, kv, H, D, T, S, W, d_in, appends):
     _case(torch_gpu, H, D, T, S, W, d_in, kv, appends, seed=300 + H * 7 + T)
