@@ -123,6 +123,32 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
     }
 
 
+def run_append_batch(torch, ll, synth, cfg, kv="bf16", window=None, n=40):
+    """n appends of one chunk issued back to back between one pair of events: the
+    kernel's own throughput, without the event bracketing of a single launch."""
+    C, T, H, D, S = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink
+    W = cfg.window if window is None else window
+    shape = (cfg.nq, H, D)
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
+    pool = [tuple(synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, t, 2000 + i) for t in range(2))
+            for i in range(POOL)]
+    for i in range((S + W + C - 1) // C + 1):
+        cache.append(0, *pool[i % POOL])
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 1)[0], _events(torch, 1)[0]
+    e0.record()
+    for i in range(n):
+        cache.append(0, *pool[i % POOL])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    rows = C * T * H
+    elt = 1 if kv != "bf16" else 2
+    byt = 2 * rows * D * 2 + 2 * rows * D * elt + (2 * rows * 4 if kv != "bf16" else 0)
+    cache.close()
+    return {"us": us, "gbs": byt / us / 1e3, "frac_hbm": byt / us / 1e3 / PEAK_HBM_GBS, "bytes": byt}
+
+
 def run_recache_layer(torch, ll, synth, cfg, reps=10):
     """Recache of one layer at the recache workload's size, bf16 and int8 caches:
     projection GEMM then rewrite (two launches, K/V round trip through HBM), and the
@@ -363,14 +389,17 @@ def main():
                                "frac_mfma": r["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r["keys"]},
             "append_bf16": {"us": r["append_us"], "gbs": r["append_gbs"],
                             "frac_hbm": r["append_gbs"] / PEAK_HBM_GBS, "bytes": r["append_bytes"]},
+            "append_bf16_back_to_back": run_append_batch(torch, ll, synth, cfg),
             "attention_int8_w21": {"ms": r8["attn_ms"], "tflops": r8["attn_tflops"],
                                    "frac_mfma": r8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r8["keys"]},
             "append_int8_w21": {"us": r8["append_us"], "gbs": r8["append_gbs"],
                                 "frac_hbm": r8["append_gbs"] / PEAK_HBM_GBS, "bytes": r8["append_bytes"]},
+            "append_int8_w21_back_to_back": run_append_batch(torch, ll, synth, cfg, "int8", i8.window),
             "attention_fp8_w21": {"ms": rf8["attn_ms"], "tflops": rf8["attn_tflops"],
                                   "frac_mfma": rf8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": rf8["keys"]},
             "append_fp8_w21": {"us": rf8["append_us"], "gbs": rf8["append_gbs"],
                                "frac_hbm": rf8["append_gbs"] / PEAK_HBM_GBS, "bytes": rf8["append_bytes"]},
+            "append_fp8_w21_back_to_back": run_append_batch(torch, ll, synth, cfg, "fp8", i8.window),
             "recache_projection": {"ms": rc["proj_ms"], "tflops": rc["proj_tflops"], "frac_mfma": rc["proj_frac"]},
             "recache_rewrite": {"us": rc["rewrite_us"], "gbs": rc["rewrite_gbs"], "frac_hbm": rc["rewrite_frac"],
                                 "bytes": rc["rewrite_bytes"]},
