@@ -62,7 +62,8 @@ typedef enum {
  * bounded; [LL-tw §六]: sink = first 3 latent frames, window = 9 latent frames.
  *
  *   layers            >= 1
- *   heads             >= 1
+ *   heads             1 .. 4096 (tile copies address a 64-row tile with 32-bit
+ *                     byte offsets)
  *   head_dim          64 or 128
  *   tokens_per_frame  >= 1 (T)
  *   sink_frames       S >= 0

@@ -16,7 +16,7 @@
 //   * K and V tiles live in LDS in their natural [key][d] layout, double-buffered,
 //     one barrier per tile.  16-byte chunks are XOR-swizzled per row so that the
 //     MFMA operand reads below are free of bank conflicts.  bf16 tiles are copied
-//     global -> LDS by the load-to-LDS path (no registers); int8 cache tiles are
+//     global -> LDS by the buffer load-to-LDS path (no registers); int8 cache tiles are
 //     widened to bf16 in registers on the way (exact for |q| <= 127).
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA: a
 //     lane then holds one query's scores for 16 keys of each 32-key block, so the
@@ -87,6 +87,21 @@ __device__ __forceinline__ int swz_row_base(int r, int c) {
   return r * D + 8 * swz<D>(r, c);
 }
 
+// One wave-wide copy global -> LDS of BYTES per lane (lane l lands at lds + BYTES l)
+// from the wave-uniform base plus the lane's byte offset voff, in the buffer form
+// (buffer_load ... lds; the offset range check is left open).  Not the global form:
+// the compiler counts a pending global-form load-to-LDS as an access to both memory
+// and LDS, and then makes every LDS read after it wait for all LDS reads in flight
+// (lgkmcnt(0)), which serialises the operand reads with the MFMAs that consume them.
+template <int BYTES>
+__device__ __forceinline__ void copy_lds(const void* base, uint32_t voff, void* lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "copy width");
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, int(voff), 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, int(voff), 0, 0, 0);
+}
+
 struct TileInfo {
   int seg;    // 0 = cache, 1 = own chunk
   int start;  // first key row of the tile within its segment
@@ -105,9 +120,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* gk, const uint16_t* gv,
     const int r0 = (wave * G::DMA_PER_WAVE + i) * G::ROWS_PER_DMA;
     const int r = r0 + lane / G::CH;
     const int c = swz<D>(r, lane % G::CH);
-    const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 8 * c;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(gk + off), (lds_void*)(lk + r0 * D), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void*)(gv + off), (lds_void*)(lv + r0 * D), 16, 0, 0);
+    const int64_t base = int64_t(ti.start) * rs;
+    const uint32_t off = uint32_t((int64_t(min(r, ti.cnt - 1)) * rs + 8 * c) * 2);
+    copy_lds<16>(gk + base, off, lk + r0 * D);
+    copy_lds<16>(gv + base, off, lv + r0 * D);
   }
 }
 
@@ -121,10 +137,8 @@ __device__ __forceinline__ void dma_full(const uint16_t* gk, const uint16_t* gv,
 #pragma unroll
   for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
     const int r0 = (wave * G::DMA_PER_WAVE + i) * G::ROWS_PER_DMA;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(gk) + loff[i]),
-                                     (lds_void*)(lk + r0 * D), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(gv) + loff[i]),
-                                     (lds_void*)(lv + r0 * D), 16, 0, 0);
+    copy_lds<16>(gk, loff[i], lk + r0 * D);
+    copy_lds<16>(gv, loff[i], lv + r0 * D);
   }
 }
 
@@ -156,15 +170,14 @@ struct QTile {
     for (int i = wave; i < COPIES; i += NW) {
       const int r0 = i * ROWS;
       const int r = r0 + lane / CH8;
-      const int64_t off = int64_t(ti.start + min(r, ti.cnt - 1)) * rs + 16 * (lane % CH8);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(gk + off), (lds_void*)(stage + r0 * D), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(gv + off), (lds_void*)(stage + STAGE + r0 * D), 16, 0, 0);
+      const int64_t base = int64_t(ti.start) * rs;
+      const uint32_t off = uint32_t(int64_t(min(r, ti.cnt - 1)) * rs + 16 * (lane % CH8));
+      copy_lds<16>(gk + base, off, stage + r0 * D);
+      copy_lds<16>(gv + base, off, stage + STAGE + r0 * D);
     }
     if (wave < 2) {
-      const float* sp = wave == 0 ? p.cKs : p.cVs;
-      const int64_t row = int64_t(ti.start + min(lane, ti.cnt - 1));
-      __builtin_amdgcn_global_load_lds((gbl_void*)(sp + row * p.H + h), (lds_void*)(wave == 0 ? lks : lvs), 4, 0,
-                                       0);
+      const float* sp = (wave == 0 ? p.cKs : p.cVs) + int64_t(ti.start) * p.H + h;
+      copy_lds<4>(sp, uint32_t(min(lane, ti.cnt - 1) * p.H * 4), wave == 0 ? lks : lvs);
     }
   }
 
@@ -700,6 +713,10 @@ struct Attn {
 #pragma unroll
       for (int e = 0; e < D / 32; ++e) O[qb][e] = f32x16{};
     }
+    // Wait for the Q fragments here, with a wait the compiler sees: their first use is
+    // inside the key walk, where it would otherwise place a memory-counter wait at the
+    // first MFMAs of every tile -- which also waits for the next tile's copies.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   }
 };
 

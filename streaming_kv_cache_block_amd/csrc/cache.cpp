@@ -154,7 +154,7 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
   if (!out) return fail(LL_ERR_INVALID, "out is NULL");
   *out = nullptr;
   if (layers < 1) return fail(LL_ERR_INVALID, "layers must be >= 1");
-  if (heads < 1) return fail(LL_ERR_INVALID, "heads must be >= 1");
+  if (heads < 1 || heads > 4096) return fail(LL_ERR_INVALID, "heads must be in [1, 4096] (got %d)", heads);
   if (head_dim != 64 && head_dim != 128) return fail(LL_ERR_INVALID, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (tokens_per_frame < 1) return fail(LL_ERR_INVALID, "tokens_per_frame must be >= 1");
   if (sink_frames < 0 || window_frames < 0 || shot_sink_frames < 0)

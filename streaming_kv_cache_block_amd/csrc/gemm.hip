@@ -10,7 +10,9 @@
 // tokens x 64 outputs with 32x32x16 bf16 MFMAs (W rows as the A operand, h rows as the
 // B operand, so a lane's accumulators hold 4 consecutive outputs of one token and the
 // bf16 results leave as 8-byte stores).  The contraction is walked in steps of TK: each
-// step's h and W tiles are copied global -> LDS with the load-to-LDS path into two
+// step's h and W tiles are copied global -> LDS with the buffer load-to-LDS path
+// (buffer_load ... lds; the global form would make the compiler wait for every LDS read
+// in flight before each MFMA, see the attention kernel's copy_lds) into two
 // buffers that are separate LDS objects (buffer parity fixed at compile time, so the
 // copy of step s+1 overlaps the MFMAs of step s).  The 16-byte chunks of a row are
 // XOR-swizzled so that the 16 rows one operand read touches land on 16 distinct bank
@@ -69,13 +71,16 @@ template <int TM, int TN, int TK, int NCOPY>
 __device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t ld, int row0, int rows_valid, int k0,
                                           uint16_t* lds, int wave, int lane) {
   using SH = Shape<TM, TN, TK>;
+  const uint16_t* base = g + int64_t(row0) * ld + k0;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, int(rows_valid * ld * 2), 0x00020000);
 #pragma unroll
   for (int i = wave; i < NCOPY; i += SH::NW) {
     const int r = SH::RPC * i + lane / SH::CPR;
     const int c = (lane % SH::CPR) ^ swz_of<TK>(r);
     const int rr = min(r, rows_valid - 1);
-    __builtin_amdgcn_global_load_lds((gbl_void*)(g + int64_t(row0 + rr) * ld + k0 + 8 * c),
-                                     (lds_void*)(lds + SH::RPC * i * TK), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + SH::RPC * i * TK), 16,
+                                             int(rr * ld + 8 * c) * 2, 0, 0, 0);
   }
 }
 
@@ -241,7 +246,7 @@ __global__ __launch_bounds__((Shape<TM, TN, TK>::NT), (Shape<TM, TN, TK>::MINB))
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int r32 = lane & 31;
   const int wm = wave & 1;     // token half

@@ -48,6 +48,7 @@ def test_create_rejects_invalid_arguments_before_touching_hip(L):
     bad = [
         (0, 12, 128, 1560, 3, 12, 0),      # layers
         (1, 0, 128, 1560, 3, 12, 0),       # heads
+        (1, 4097, 64, 16, 3, 12, 0),       # heads beyond the tile copies' 32-bit offsets
         (1, 12, 96, 1560, 3, 12, 0),       # head_dim
         (1, 12, 128, 0, 3, 12, 0),         # tokens per frame
         (1, 12, 128, 1560, -1, 12, 0),     # negative sink
