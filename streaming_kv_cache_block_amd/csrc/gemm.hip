@@ -16,10 +16,8 @@
 // buffers that are separate LDS objects (buffer parity fixed at compile time, so the
 // copy of step s+1 overlaps the MFMAs of step s).  The 16-byte chunks of a row are
 // XOR-swizzled so that the 16 rows one operand read touches land on 16 distinct bank
-// groups.  Output counts that are a multiple of 256 use 192 x 256 tiles, TK = 64, 8
-// waves and one workgroup per CU; others 256 x 128, TK = 32, 4 waves, two workgroups
-// per CU.  Each unit is one (token tile, output tile, K or V) triple; workgroups that
-// share an h tile run on the same XCD.
+// groups.  Tile shapes are listed at Shape below.  Each unit is one (token tile, output
+// tile, K or V) triple; workgroups that share an h tile run on the same XCD.
 #include <type_traits>
 
 #include "device_common.h"
@@ -30,13 +28,16 @@ namespace {
 
 constexpr int NXCD = 8;
 
-// Tile shapes: TM tokens x TN outputs per workgroup of 2 TN / 64 waves (each TM / 2
-// tokens x 64 outputs), contraction steps of TK.  TN = 256, TK = 64 (8 waves, one
-// workgroup per CU, up to 128 KB of LDS) halves the global -> LDS bytes per MFMA of
-// TN = 128, TK = 32 (4 waves, two workgroups per CU) and the barriers per contraction
-// length; the smaller shape serves output counts that are not a multiple of 256.
-template <int TM, int TN, int TK>
+// Tile shapes: TM tokens x TN outputs per workgroup of 2 TN / 64 waves, each TM / 2
+// tokens x 64 outputs, contraction steps of TK, MINB workgroups per CU.  The larger the
+// tile, the more multiply-adds each byte copied global -> LDS feeds, which is what
+// bounds this kernel: 192 x 384 with TK = 64 (12 waves, three per SIMD, 144 KB of
+// double-buffered LDS) for output counts that are a multiple of 384, 192 x 256 (8
+// waves, 112 KB) for other multiples of 256, 256 x 128 with TK = 32 (4 waves, two
+// workgroups per CU) for the rest.
+template <int TM_, int TN_, int TK_, int MINB_>
 struct Shape {
+  static constexpr int TM = TM_, TN = TN_, TK = TK_, MINB = MINB_;
   static constexpr int MB = TM / 64;                 // 32-token blocks per wave
   static constexpr int WM = TM / 2;                  // tokens per wave
   static constexpr int NW = 2 * TN / 64;             // waves
@@ -45,7 +46,6 @@ struct Shape {
   static constexpr int WCOPY = TN * TK * 2 / 1024;   // of the W tile
   static constexpr int CPR = TK / 8;                 // 16-byte chunks per row
   static constexpr int RPC = 64 / CPR;               // rows per wave-wide copy
-  static constexpr int MINB = TN == 128 ? 2 : 1;     // workgroups per CU
   static_assert(HCOPY % NW == 0 && WCOPY % NW == 0, "copies per wave");
 };
 
@@ -67,10 +67,10 @@ __device__ __forceinline__ int gswz(int r, int c) { return r * TK + 8 * (c ^ swz
 // Copy rows [0, rows) x [k0, k0 + TK) of a row-major [*, ld] bf16 matrix into LDS.
 // Lane l of copy i fills LDS bytes [1 KB i + 16 l, +16): row RPC i + l / CPR, chunk
 // position l % CPR, which holds source chunk (l % CPR) ^ swz(row).
-template <int TM, int TN, int TK, int NCOPY>
+template <class SH, int NCOPY>
 __device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t ld, int row0, int rows_valid, int k0,
                                           uint16_t* lds, int wave, int lane) {
-  using SH = Shape<TM, TN, TK>;
+  constexpr int TK = SH::TK;
   const uint16_t* base = g + int64_t(row0) * ld + k0;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, int(rows_valid * ld * 2), 0x00020000);
@@ -99,17 +99,16 @@ __device__ __forceinline__ int64_t slot_row(int m, int T, const int* plan) {
 // per row and a Markstein FMA correction; plain division where the absmax is below
 // 2^-100 or above 2^120).  x is the bf16-rounded sum, exactly what a separate
 // projection would have stored.
-template <int EPI, int TM, int TN, int TK>
-__device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc,
-                                               const f32x16 (&acc)[2][Shape<TM, TN, TK>::MB], int m0, int n0,
-                                               int z, int wm, int wn, int g, int r32, int tid) {
-  constexpr int MB = Shape<TM, TN, TK>::MB, WM = Shape<TM, TN, TK>::WM;
+template <int EPI, class SH>
+__device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, const f32x16 (&acc)[2][SH::MB], int m0,
+                                               int n0, int z, int wm, int wn, int g, int r32, int tid) {
+  constexpr int MB = SH::MB, WM = SH::WM, TN = SH::TN;
   // A frame may be held by two slots (a shot-sink frame still in the window): the row
   // is then written to both.
   __shared__ int plan[kMaxPlan], plan2[kMaxPlan];
   __shared__ float amax[2][TN / 64][WM];   // [wm][wn][token within the wave's half]
   const ProjParams& p = pc.proj;
-  for (int i = tid; i < pc.n_plan; i += Shape<TM, TN, TK>::NT) {
+  for (int i = tid; i < pc.n_plan; i += SH::NT) {
     plan[i] = pc.plan_slot[i];
     plan2[i] = pc.plan_slot2[i];
   }
@@ -222,10 +221,9 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc,
 
 // EPI 0: plain [M][N] outputs; 1: bf16 rows into cache slots; 2: int8 rows + scales;
 // 3: fp8 (E4M3) rows + scales.
-template <int EPI, int TM, int TN, int TK>
-__global__ __launch_bounds__((Shape<TM, TN, TK>::NT), (Shape<TM, TN, TK>::MINB)) void proj_kernel(
-    const ProjToCacheParams pc, int n_mt, int n_units) {
-  using SH = Shape<TM, TN, TK>;
+template <int EPI, class SH>
+__global__ __launch_bounds__(SH::NT, SH::MINB) void proj_kernel(const ProjToCacheParams pc, int n_mt, int n_units) {
+  constexpr int TM = SH::TM, TN = SH::TN, TK = SH::TK;
   constexpr int MB = SH::MB, WM = SH::WM;
   const ProjParams& p = pc.proj;
   __shared__ __attribute__((aligned(1024))) uint16_t sh0[TM * TK];
@@ -265,8 +263,8 @@ __global__ __launch_bounds__((Shape<TM, TN, TK>::NT), (Shape<TM, TN, TK>::MINB))
 
   auto issue = [&](auto pb, int k0) __attribute__((always_inline)) {
     constexpr int PB = decltype(pb)::value;
-    copy_tile<TM, TN, TK, SH::HCOPY>(p.h, p.K, m0, m_valid, k0, PB ? sh1 : sh0, wave, lane);
-    copy_tile<TM, TN, TK, SH::WCOPY>(W, p.K, n0, TN, k0, PB ? sw1 : sw0, wave, lane);
+    copy_tile<SH, SH::HCOPY>(p.h, p.K, m0, m_valid, k0, PB ? sh1 : sh0, wave, lane);
+    copy_tile<SH, SH::WCOPY>(W, p.K, n0, TN, k0, PB ? sw1 : sw0, wave, lane);
   };
   auto compute = [&](auto pb) __attribute__((always_inline)) {
     constexpr int PB = decltype(pb)::value;
@@ -324,21 +322,20 @@ __global__ __launch_bounds__((Shape<TM, TN, TK>::NT), (Shape<TM, TN, TK>::MINB))
         }
     }
   } else {
-    cache_epilogue<EPI, TM, TN, TK>(pc, acc, m0, n0, z, wm, wn, g, r32, tid);
+    cache_epilogue<EPI, SH>(pc, acc, m0, n0, z, wm, wn, g, r32, tid);
   }
 }
 
 }  // namespace
 
 namespace {
-template <int EPI, int TM, int TN, int TK>
+template <int EPI, class SH>
 hipError_t launch_shape(const ProjToCacheParams& pc, hipStream_t s) {
   const ProjParams& p = pc.proj;
-  const int n_mt = (p.M + TM - 1) / TM;
-  const int n_units = n_mt * (p.N / TN) * 2;
+  const int n_mt = (p.M + SH::TM - 1) / SH::TM;
+  const int n_units = n_mt * (p.N / SH::TN) * 2;
   const int grid = (n_units + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL((proj_kernel<EPI, TM, TN, TK>), dim3(grid), dim3(Shape<TM, TN, TK>::NT), 0, s, pc, n_mt,
-                     n_units);
+  hipLaunchKernelGGL((proj_kernel<EPI, SH>), dim3(grid), dim3(SH::NT), 0, s, pc, n_mt, n_units);
   return hipGetLastError();
 }
 
@@ -346,11 +343,13 @@ template <int EPI>
 hipError_t launch_proj(const ProjToCacheParams& pc, hipStream_t s) {
   const ProjParams& p = pc.proj;
   if (p.K % 64 != 0 || p.N % 128 != 0 || p.M <= 0) return hipErrorInvalidValue;
-  // 192 tokens per workgroup in the large shape: at the recache size (23400 tokens x
-  // 3072 outputs) the 122 x 12 units fill 256 CUs in 5.7 rounds where 256-token tiles
-  // take 4.3 rounds and idle 70% of the chip in the last one (measured 1.6% faster).
-  if (p.N % 256 == 0) return launch_shape<EPI, 192, 256, 64>(pc, s);
-  return launch_shape<EPI, 256, 128, 32>(pc, s);
+  // 192 x 384 tiles at the recache size (23400 tokens x 2 x 1536 outputs): 122 x 8
+  // units fill 256 CUs in 3.8 rounds, and each copied byte feeds 64 multiply-adds
+  // (55 for 192 x 256; 256-token tiles would leave most of the chip idle in the last
+  // round).
+  if (p.N % 384 == 0) return launch_shape<EPI, Shape<192, 384, 64, 1>>(pc, s);
+  if (p.N % 256 == 0) return launch_shape<EPI, Shape<192, 256, 64, 1>>(pc, s);
+  return launch_shape<EPI, Shape<256, 128, 32, 2>>(pc, s);
 }
 }  // namespace
 
