@@ -89,6 +89,8 @@ def _case(torch, H, D, T, S, W, d_in, kv, appends, seed):
     (2, 128, 17, 1, 3, 64, [2, 2]),            # 256 outputs (wide tiles), one 64-wide contraction step
     (1, 128, 9, 2, 2, 64, [1, 3]),             # 128 outputs, two 32-wide contraction steps
     (4, 128, 100, 2, 4, 128, [3, 3, 3]),       # 512 outputs (two wide output tiles), 600 tokens
+    (6, 64, 20, 2, 3, 128, [2, 3]),            # 384 outputs of head_dim 64 (one 192 x 384 tile)
+    (6, 128, 24, 1, 3, 192, [2, 2]),           # 768 outputs (two 192 x 384 tiles)
 ])
 def test_fused_recache_matches_project_then_recache(torch_gpu, kv, H, D, T, S, W, d_in, appends):
     _case(torch_gpu, H, D, T, S, W, d_in, kv, appends, seed=300 + H * 7 + T)

@@ -79,11 +79,17 @@ def test_projection_identity_and_small_integers_bit_exact(torch_gpu):
     eye = bf16.round_f32(np.eye(d, dtype=np.float32))
     K, V = ll.kv_project(synth.to_device(h), synth.to_device(eye), synth.to_device(eye))
     assert np.array_equal(synth.to_bits(K), h) and np.array_equal(synth.to_bits(V), h)
+    # small integers: every fp32 partial sum is exact, so the bf16 outputs are unique.
+    # 128, 384 and 768 outputs take the three tile shapes (256 x 128, 192 x 384 once
+    # and twice); 777 tokens leave a ragged token tile in each.
     rng = np.random.default_rng(4)
     hi = bf16.round_f32(rng.integers(-8, 9, size=(n, 192)).astype(np.float32))
-    wi = bf16.round_f32(rng.integers(-8, 9, size=(128, 192)).astype(np.float32))
-    K, _ = ll.kv_project(synth.to_device(hi), synth.to_device(wi), synth.to_device(wi))
-    assert np.array_equal(synth.to_bits(K), gemm.project_bf16(hi, wi))
+    for d_out in (128, 384, 768):
+        wi = bf16.round_f32(rng.integers(-8, 9, size=(d_out, 192)).astype(np.float32))
+        K, V = ll.kv_project(synth.to_device(hi), synth.to_device(wi), synth.to_device(wi))
+        want = gemm.project_bf16(hi, wi)
+        assert np.array_equal(synth.to_bits(K), want), d_out
+        assert np.array_equal(synth.to_bits(V), want), d_out
 
 
 def _projection_bound_violations(got_bits, h_bits, w_bits):
