@@ -50,7 +50,6 @@ struct Shape {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 // Chunk swizzle of row r: the 16 rows one operand read serves together land on 16
 // distinct 16-byte bank groups (64-byte rows: r >> 2; 128-byte rows: r >> 1, the row
