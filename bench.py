@@ -123,6 +123,27 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
     }
 
 
+def run_copy_reference(torch, cfg, n=40):
+    """Context for the append: the runtime's own device-to-device copy of the same bytes
+    (one chunk's K and V, one launch per step like the append), issued back to back and
+    timed like run_append_batch."""
+    rows = cfg.nq * cfg.heads * cfg.head_dim
+    src = torch.empty(2 * rows, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 1)[0], _events(torch, 1)[0]
+    e0.record()
+    for _ in range(n):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    byt = 2 * 2 * rows * 2
+    return {"us": us, "gbs": byt / us / 1e3, "frac_hbm": byt / us / 1e3 / PEAK_HBM_GBS, "bytes": byt}
+
+
 def run_append_batch(torch, ll, synth, cfg, kv="bf16", window=None, n=40):
     """n appends of one chunk issued back to back between one pair of events: the
     kernel's own throughput, without the event bracketing of a single launch."""
@@ -390,6 +411,7 @@ def main():
             "append_bf16": {"us": r["append_us"], "gbs": r["append_gbs"],
                             "frac_hbm": r["append_gbs"] / PEAK_HBM_GBS, "bytes": r["append_bytes"]},
             "append_bf16_back_to_back": run_append_batch(torch, ll, synth, cfg),
+            "copy_reference_same_bytes": run_copy_reference(torch, cfg),
             "attention_int8_w21": {"ms": r8["attn_ms"], "tflops": r8["attn_tflops"],
                                    "frac_mfma": r8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r8["keys"]},
             "append_int8_w21": {"us": r8["append_us"], "gbs": r8["append_gbs"],

@@ -7,7 +7,10 @@
 // Eviction is the overwrite of a ring slot; no memory is allocated or freed.
 //
 // bf16 caches: a frame is one contiguous run of T*H*D bf16 in both the source and the
-// slot, so this is a streaming 16-byte-vector copy (HBM bound).
+// slot, so this is a streaming 16-byte-vector copy (HBM bound).  Plain loads and
+// non-temporal (streaming) stores: measured on gfx950 against the other three
+// combinations of the two hints, this one moves the append's 57.5 MB fastest, faster
+// than the runtime's own device copy; non-temporal loads were the slow part.
 // int8 caches: each (token, head) row of D values is quantised on the fly
 //   a = max |x|, scale = a / 127, q = clamp(rint((x * 127) / a), -127, 127)
 // (every operation IEEE binary32, correctly rounded quotient, ties-to-even rounding;
@@ -36,12 +39,12 @@ __global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t i = base + int64_t(u) * kThreads;
-    if (i < vecs_per_frame) r[u] = __builtin_nontemporal_load(src + i);
+    if (i < vecs_per_frame) r[u] = src[i];
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t i = base + int64_t(u) * kThreads;
-    if (i < vecs_per_frame) dst[i] = r[u];
+    if (i < vecs_per_frame) __builtin_nontemporal_store(r[u], dst + i);
   }
 }
 
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
 #pragma unroll
   for (int rr = 0; rr < RPG; ++rr) {
     const int64_t row = row0 + rr;
-    w[rr] = row < p.rows_per_frame ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * D + 8 * sub))
+    w[rr] = row < p.rows_per_frame ? *reinterpret_cast<const u32x4*>(src + row * D + 8 * sub)
                                    : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
@@ -128,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
       }
     }
     if (row < p.rows_per_frame) {
-      *reinterpret_cast<u32x2*>(dst + row * D + 8 * sub) = u32x2{packed[0], packed[1]};
-      if (sub == 0) dsc[row] = scale;
+      __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, reinterpret_cast<u32x2*>(dst + row * D + 8 * sub));
+      if (sub == 0) __builtin_nontemporal_store(scale, dsc + row);
     }
   }
 }
