@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
     }
     if (row < p.rows_per_frame) {
       __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, reinterpret_cast<u32x2*>(dst + row * D + 8 * sub));
-      if (sub == 0) __builtin_nontemporal_store(scale, dsc + row);
+      if (sub == 0) dsc[row] = scale;   // 4-byte scales of adjacent rows merge in the L2
     }
   }
 }
