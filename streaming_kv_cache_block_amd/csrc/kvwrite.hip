@@ -9,8 +9,9 @@
 // bf16 caches: a frame is one contiguous run of T*H*D bf16 in both the source and the
 // slot, so this is a streaming 16-byte-vector copy (HBM bound).  Plain loads and
 // non-temporal (streaming) stores: measured on gfx950 against the other three
-// combinations of the two hints, this one moves the append's 57.5 MB fastest, faster
-// than the runtime's own device copy; non-temporal loads were the slow part.
+// combinations of the two hints, this one moves the append's 57.5 MB fastest, at the
+// speed of the runtime's own device copy of the same bytes; non-temporal loads were
+// the slow part.
 // int8 caches: each (token, head) row of D values is quantised on the fly
 //   a = max |x|, scale = a / 127, q = clamp(rint((x * 127) / a), -127, 127)
 // (every operation IEEE binary32, correctly rounded quotient, ties-to-even rounding;
