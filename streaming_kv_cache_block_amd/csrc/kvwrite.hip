@@ -124,11 +124,16 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
           packed[w] = f32x2_to_e4m3x2(qq[4 * w + 2], qq[4 * w + 3], packed[w], true);
         }
       } else {
+        // q = clamp(rint(quotient), -127, 127) is an integer, so q + 128 in [1, 255] is
+        // exact and converts exactly to an unsigned byte; flipping bit 7 of each byte
+        // then gives the two's-complement code of q.
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int qi = int(fminf(fmaxf(__builtin_rintf(qq[k]), -127.0f), 127.0f));
-          packed[k >> 2] |= (uint32_t(qi) & 0xffu) << (8 * (k & 3));
+          const float t = __builtin_amdgcn_fmed3f(__builtin_rintf(qq[k]), -127.0f, 127.0f) + 128.0f;
+          packed[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(t, k & 3, packed[k >> 2]);
         }
+        packed[0] ^= 0x80808080u;
+        packed[1] ^= 0x80808080u;
       }
     }
     if (row < p.rows_per_frame) {
