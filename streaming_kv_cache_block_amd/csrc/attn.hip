@@ -16,8 +16,9 @@
 //   * K and V tiles live in LDS in their natural [key][d] layout, double-buffered,
 //     one barrier per tile.  16-byte chunks are XOR-swizzled per row so that the
 //     MFMA operand reads below are free of bank conflicts.  bf16 tiles are copied
-//     global -> LDS by the buffer load-to-LDS path (no registers); int8 cache tiles are
-//     widened to bf16 in registers on the way (exact for |q| <= 127).
+//     global -> LDS by the buffer load-to-LDS path (no registers); int8 / fp8 cache
+//     tiles are copied as codes into a per-wave staging area the same way and widened
+//     to bf16 by that wave (exact: |q| <= 127, and every E4M3 value is a bf16 value).
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA: a
 //     lane then holds one query's scores for 16 keys of each 32-key block, so the
 //     running row max needs one register exchange with lane ^ 32
@@ -32,8 +33,8 @@
 //     Full bf16 tiles first take the probabilities against the running max as it
 //     stands and check the bound on the lane's tile sum; only tiles that fail it
 //     (rare after the first) compute the tile max, rescale and take them again.
-//   * int8 caches: the per-key K scale multiplies the score column and the V scale
-//     the probability column before rounding to bf16 (LongLive-2.0 explainer,
+//   * int8 / fp8 caches: the per-key K scale multiplies the score column and the V
+//     scale the probability column before rounding to bf16 (LongLive-2.0 explainer,
 //     wmrh.cn, §15.3: dequantisation fused into the consumer, not a separate pass).
 //   * Workgroups are numbered so that the query tiles of one head run on the same
 //     XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs) and share
