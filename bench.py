@@ -63,7 +63,9 @@ def _attn_flops(H, D, nq, nk):
 
 
 def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
-    """The timed step loop; returns a dict of measurements."""
+    """The timed step loop (nothing but the steps between the two synchronisations),
+    then as many steps again with HIP events around each launch for the per-kernel
+    times; returns a dict of measurements."""
     kv = kv or ("int8" if kv_int8 else "bf16")
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     shape = (cfg.nq, H, D)
@@ -102,9 +104,12 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
     assert min(cache.frames_seen(0), S + W) == n_vis
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, True)
+        step(i, False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
     attn_ms = [a0[j].elapsed_time(a1[j]) for j in range(steps * P)]
     app_ms = [b0[i].elapsed_time(b1[i]) for i in range(steps)]
     elt = 1 if kv != "bf16" else 2
