@@ -21,8 +21,11 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     device work of a call is enqueued on it; nothing blocks the host.
  *   - Host-side bookkeeping (frames seen f0, which frame each slot holds) is
- *     updated when a call is enqueued, so calls on one cache must be issued in
- *     stream order and must not race from several host threads.
+ *     kept per layer and updated when a call is enqueued.  Calls on ONE layer must
+ *     be issued in stream order (one stream, or streams the caller orders with
+ *     events) and from one host thread at a time.  Different layers may be used
+ *     from different streams and host threads at the same time: each layer has
+ *     its own slots, bookkeeping and attention work area.
  *   - Every function returns a status; no exception or abort crosses the ABI.
  *     Arguments are validated BEFORE any HIP call: LL_ERR_INVALID for bad
  *     arguments, LL_ERR_STATE for calls the cache's state forbids, LL_ERR_OOM when
@@ -82,12 +85,14 @@ typedef enum {
  *                     Every division above is one IEEE binary32 division.
  *   out               receives the handle
  *
- * Device memory: layers * 2 * (S+W) * T * heads * head_dim * (2 or 1) bytes, plus
- * layers * 2 * (S+W) * T * heads * 4 bytes of scales for int8 / fp8, plus a fixed
- * attention work area (partial results of split key walks: 3 * CUs * 256 rows *
- * (head_dim + 2) * 4 bytes, about 100 MB for head_dim 128 on 256 CUs).  Slot contents
- * start undefined; no slot is visible until written.  Errors: LL_ERR_INVALID,
- * LL_ERR_OOM, LL_ERR_HIP.
+ * Device memory, one allocation made here (no later call allocates):
+ * layers * 2 * (S+W) * T * heads * head_dim * (2 or 1) bytes of slots, plus
+ * layers * 2 * (S+W) * T * heads * 4 bytes of scales for int8 / fp8, plus per layer
+ * an attention work area for split key walks (2 * CUs partial results of 256 rows *
+ * (head_dim + 2) * 4 bytes and CUs arrival counters: about 68 MB for head_dim 128 on
+ * 256 CUs).  Slot contents start undefined; no slot is visible until written.  The
+ * call waits only for the zeroing of its own counters (a private stream).
+ * Errors: LL_ERR_INVALID, LL_ERR_OOM, LL_ERR_HIP.
  */
 ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_frame,
                           int sink_frames, int window_frames, int kv_dtype,
@@ -227,7 +232,8 @@ ll_status ll_cache_recache_from_hidden(ll_cache *c, int layer, const void *h, co
 ll_status ll_cache_frames_seen(const ll_cache *c, int layer, int64_t *f0);
 
 /* For each of the S+Ss+W slots of `layer`, the frame it holds, or -1 if empty.
- * frame_of_slot must have room for S+W entries (host memory). */
+ * frame_of_slot must have room for S+Ss+W entries (host memory; S+W without a
+ * shot sink). */
 ll_status ll_cache_slot_frames(const ll_cache *c, int layer, int64_t *frame_of_slot);
 
 /* Device pointers of `layer`'s slot arrays (read them after synchronising):

@@ -53,7 +53,8 @@ def quantize(x):
     a = np.abs(x).max(axis=-1)                       # exact
     scale = (a / _F127).astype(np.float32)           # binary32 division
     safe_a = np.where(a == 0, np.float32(1.0), a).astype(np.float32)
-    r = np.rint((x * _F127) / safe_a[..., None])      # binary32 ops, ties to even
+    with np.errstate(over="ignore"):                  # x * 127 may overflow to +-inf; the clip saturates it
+        r = np.rint((x * _F127) / safe_a[..., None])  # binary32 ops, ties to even
     r = np.clip(r, -127, 127)
     q = np.where((a == 0)[..., None], 0, r).astype(np.int8)
     return q, scale

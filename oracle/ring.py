@@ -26,6 +26,14 @@ sink frames [0, min(S, f0)) in ascending order followed by the window frames
 [max(S, f0 - W), f0) oldest to newest; block idx of the recache tensors
 replaces frame list[idx] in slot(list[idx]).  f0 is unchanged.
 
+``recache_window(n)`` is the narrower recache of the techwalker.com article,
+§六 (recomputation limited to the most recent window, the sink tokens kept as
+they are).  Its logical list is the window frames alone, [max(S, f0 - W), f0)
+oldest to newest, and n must equal its length (at least 1); block idx replaces
+frame list[idx] in every slot that holds it.  Sink slots (and, with a shot
+sink, shot-sink frames that have left the window) keep their bytes; f0 is
+unchanged.
+
 Each slot records which frame it holds (``slot_frame``, -1 = empty) and a
 caller-defined token for where its bytes came from (``slot_src``), so tests
 can compare GPU slot bytes with the bytes of the frame the model says are
@@ -99,6 +107,22 @@ class RingModel:
         frames = self.retained_frames()
         if n != len(frames):
             raise ValueError("recache: n must equal the number of retained frames")
+        for idx, f in enumerate(frames):
+            held = [s for s, g in enumerate(self.slot_frame) if g == f]
+            if not held:
+                raise AssertionError("ring model inconsistent")
+            for s in held:
+                self.slot_src[s] = src_of_block(idx)
+
+    def window_frames(self) -> list:
+        """Logical order of the window-only recache: the non-sink frames of the most
+        recent window, oldest -> newest."""
+        return list(range(max(self.S, self.f0 - self.W), self.f0))
+
+    def recache_window(self, n: int, src_of_block=lambda idx: idx):
+        frames = self.window_frames()
+        if n != len(frames) or n == 0:
+            raise ValueError("recache_window: n must equal the number of window frames (>= 1)")
         for idx, f in enumerate(frames):
             held = [s for s, g in enumerate(self.slot_frame) if g == f]
             if not held:

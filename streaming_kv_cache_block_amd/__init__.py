@@ -138,35 +138,57 @@ class Cache:
     def _frames(self, t, n_frames):
         if n_frames is not None:
             return n_frames
+        if isinstance(t, int):
+            raise ValueError("n_frames is required with raw pointers")
         rows = t.shape[0]
         if rows % self.T:
             raise ValueError("tensor rows are not a whole number of frames")
         return rows // self.T
 
+    def _tokens(self, n_frames, **tensors):
+        """Each token tensor must hold exactly n_frames*T*heads*head_dim elements, so the
+        kernels never read or write past it (raw integer pointers are the caller's
+        responsibility)."""
+        want = n_frames * self.T * self.heads * self.head_dim
+        for name, t in tensors.items():
+            if t is not None and not isinstance(t, int) and t.numel() != want:
+                raise ValueError(f"{name} has {t.numel()} elements; {n_frames} frames x {self.T} tokens x "
+                                 f"{self.heads} heads x {self.head_dim} need {want}")
+        return n_frames
+
     def append(self, layer, K, V, n_frames=None, stream=None):
-        _check(lib().ll_cache_append(self._h, layer, _ptr(K), _ptr(V), self._frames(K, n_frames),
-                                     _stream(stream)))
+        n = self._tokens(self._frames(K, n_frames), K=K, V=V)
+        _check(lib().ll_cache_append(self._h, layer, _ptr(K), _ptr(V), n, _stream(stream)))
 
     def attn(self, layer, Q, K_chunk, V_chunk, out=None, n_frames=None, stream=None):
         if out is None:
             import torch
             out = torch.empty_like(Q)
-        _check(lib().ll_attn_sink_window(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk),
-                                         self._frames(Q, n_frames), _ptr(out), _stream(stream)))
+        n = self._tokens(self._frames(Q, n_frames), Q=Q, K_chunk=K_chunk, V_chunk=V_chunk, out=out)
+        _check(lib().ll_attn_sink_window(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n, _ptr(out),
+                                         _stream(stream)))
         return out
 
     def recache(self, layer, K_all, V_all, n_frames=None, stream=None):
-        _check(lib().ll_cache_recache(self._h, layer, _ptr(K_all), _ptr(V_all),
-                                      self._frames(K_all, n_frames), _stream(stream)))
+        n = self._tokens(self._frames(K_all, n_frames), K_all=K_all, V_all=V_all)
+        _check(lib().ll_cache_recache(self._h, layer, _ptr(K_all), _ptr(V_all), n, _stream(stream)))
 
     def recache_window(self, layer, K_win, V_win, n_frames=None, stream=None):
-        _check(lib().ll_cache_recache_window(self._h, layer, _ptr(K_win), _ptr(V_win),
-                                             self._frames(K_win, n_frames), _stream(stream)))
+        n = self._tokens(self._frames(K_win, n_frames), K_win=K_win, V_win=V_win)
+        _check(lib().ll_cache_recache_window(self._h, layer, _ptr(K_win), _ptr(V_win), n, _stream(stream)))
 
     def recache_from_hidden(self, layer, h, W_K, W_V, n_frames=None, stream=None):
         """Recache from hidden states h [n_frames*T][d_in]: K/V = h W^T written into the slots."""
-        _check(lib().ll_cache_recache_from_hidden(self._h, layer, _ptr(h), _ptr(W_K), _ptr(W_V),
-                                                  self._frames(h, n_frames), h.shape[1], _stream(stream)))
+        n = self._frames(h, n_frames)
+        d_in = h.shape[1]
+        d_out = self.heads * self.head_dim
+        if h.numel() != n * self.T * d_in:
+            raise ValueError(f"h must be [{n * self.T}][{d_in}], got {tuple(h.shape)}")
+        for name, w in (("W_K", W_K), ("W_V", W_V)):
+            if w.numel() != d_out * d_in:
+                raise ValueError(f"{name} must be [{d_out}][{d_in}], got {tuple(w.shape)}")
+        _check(lib().ll_cache_recache_from_hidden(self._h, layer, _ptr(h), _ptr(W_K), _ptr(W_V), n, d_in,
+                                                  _stream(stream)))
 
     def begin_shot(self, layer):
         _check(lib().ll_cache_begin_shot(self._h, layer))
@@ -238,6 +260,12 @@ def kv_project(h, W_K, W_V, K_all=None, V_all=None, stream=None):
     import torch
     n, d_in = h.shape
     d_out = W_K.shape[0]
+    for name, w in (("W_K", W_K), ("W_V", W_V)):
+        if tuple(w.shape) != (d_out, d_in):
+            raise ValueError(f"{name} must be [{d_out}][{d_in}], got {tuple(w.shape)}")
+    for name, t in (("K_all", K_all), ("V_all", V_all)):
+        if t is not None and t.numel() != n * d_out:
+            raise ValueError(f"{name} must hold {n} x {d_out} elements, got {t.numel()}")
     if K_all is None:
         K_all = torch.empty((n, d_out), dtype=torch.bfloat16, device=h.device)
     if V_all is None:

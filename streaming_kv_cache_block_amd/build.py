@@ -71,9 +71,10 @@ def build(verbose: bool = False) -> str:
 
 
 def build_slots_cli() -> str:
-    """Host-only build of the slot-math driver (g++, address + UB sanitizers)."""
+    """Host-only build of the slot-math and split-plan driver (g++, address + UB
+    sanitizers, LL_DEBUG bounds checks)."""
     os.makedirs(BUILD, exist_ok=True)
-    _run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+    _run(["g++", "-std=c++17", "-O1", "-g", "-DLL_DEBUG", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
           "-I", CSRC, os.path.join(CSRC, "slots_cli.cpp"), "-o", SLOTS_CLI])
     return SLOTS_CLI
 

@@ -48,16 +48,7 @@ namespace ll {
 namespace {
 
 constexpr int BN = 64;         // keys per tile
-constexpr int NXCD = 8;
 constexpr float kLazyThreshold = 8.0f;   // log2 units
-#ifndef LL_PIECE_TILES
-#define LL_PIECE_TILES 12
-#endif
-constexpr int kPieceTiles = LL_PIECE_TILES;   // per-piece overhead of a split walk, in tiles
-#ifndef LL_SPEC
-#define LL_SPEC 1
-#endif
-constexpr bool kSpecSoftmax = LL_SPEC;   // full bf16 tiles: probabilities against the running max first
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -591,7 +582,7 @@ struct Attn {
   template <bool MASK, bool SCALED>
   __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lks, const float* lvs,
                                        int cnt, bool scaled = SCALED) {
-    if constexpr (kSpecSoftmax && !MASK && !SCALED) {
+    if constexpr (!MASK && !SCALED) {
       tile_spec(lk, lv);
     } else {
       f32x16 S[NQB][2];
@@ -721,28 +712,6 @@ struct Attn {
   }
 };
 
-// Per-XCD work plan of a split launch: blocks [b0, b0 + nb) run on this XCD, one
-// workgroup each for their first J - t tiles; ns spare workgroups take the tails, spare
-// s the tail units [s L, (s + 1) L) of the XCD (unit = one tile of one block's tail,
-// block-major).  L >= t, so a tail meets at most two spares and a block has at most
-// three pieces.
-struct XcdPlan {
-  int b0 = 0, nb = 0, ns = 0, t = 0, L = 0;
-  XcdPlan() = default;
-  __host__ __device__ XcdPlan(const Split& sp, int x) {
-    b0 = x * sp.B / NXCD;
-    nb = (x + 1) * sp.B / NXCD - b0;
-    ns = sp.per_xcd - nb;
-    // heads walk J - t tiles; a spare walks about nb t / ns tiles over about nb / ns + 1
-    // pieces, each costing ~kPieceTiles tiles of set-up and hand-over: equal times at
-    // t = J ns / (nb + ns) - kPieceTiles.
-    t = ns > 0 ? max(0, sp.J * ns / (nb + ns) - kPieceTiles) : 0;
-    L = t ? (nb * t + ns - 1) / ns : 0;
-  }
-  __host__ __device__ int first_spare(int b) const { return b * t / L; }
-  __host__ __device__ int n_tail(int b) const { return ((b + 1) * t - 1) / L - b * t / L + 1; }
-};
-
 template <int D, int NQB, int NW, int MINB, int KVQ, bool RUNS>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p, const Split sp) {
   using G = Geo<D, NW>;
@@ -772,7 +741,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
 
   // RUNS: the cached context may be several runs of slots (shot sink)
   const std::conditional_t<RUNS, TileOrderN, TileOrder1> order(p);
-  const int ntiles = order.total();
   uint32_t loff[Geo<D, NW>::DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < Geo<D, NW>::DMA_PER_WAVE; ++i) loff[i] = dma_lane_offset<D, NW>(rs, wave, lane, i);
@@ -781,7 +749,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   // one of the block's npc pieces.  A whole block stores its output; otherwise the piece
   // leaves a partial result in its slot and the last piece of the block to arrive
   // merges them all.
-  auto piece = [&](int blk, int ja, int jb, int npc, int slot) __attribute__((always_inline)) {
+  auto piece = [&](const Piece& pc) __attribute__((always_inline)) {
+    const int blk = pc.blk, ja = pc.ja, jb = pc.jb, npc = pc.npc, slot = pc.slot;
     const int h = blk / sp.n_qtiles;
     const int q0 = (blk % sp.n_qtiles) * ROWS + wave * (32 * NQB);
     const int jend = jb;
@@ -877,7 +846,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
     // A piece that finds every other piece already counted is the last one: it merges
     // from its registers without leaving a partial (the common case for the head piece,
     // which has the longest walk).
-    const int64_t slot_floats = split_slot_floats(D, ROWS);
+    const int64_t slot_floats = split_slot_floats(D, kAttnRows);
     if (tid == 0) sm_last = coherent_load(sp.cnt + blk) == npc - 1;
     __syncthreads();
     if (!sm_last) {
@@ -888,58 +857,26 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
       __syncthreads();
     }
     if (sm_last) {
-      // the block's pieces in order: blk (head piece), B + 2 blk + k (tail pieces)
-      const int own = slot == blk ? 0 : slot - (sp.B + 2 * blk) + 1;
-      A.merge_store(sp.ws + int64_t(blk) * slot_floats, sp.ws + int64_t(sp.B + 2 * blk) * slot_floats,
-                    sp.ws + int64_t(sp.B + 2 * blk + 1) * slot_floats, own, npc, ROWS, wave, p.out, q0, p.nq, rs,
+      // the block's pieces in order: blk (head piece), tail0 + k (tail pieces)
+      const int own = slot == blk ? 0 : slot - pc.tail0 + 1;
+      A.merge_store(sp.ws + int64_t(blk) * slot_floats, sp.ws + int64_t(pc.tail0) * slot_floats,
+                    sp.ws + int64_t(pc.tail0 + 1) * slot_floats, own, npc, ROWS, wave, p.out, q0, p.nq, rs,
                     h);
       if (tid == 0) coherent_store(sp.cnt + blk, 0);   // ready for the next call on the stream
     }
     __syncthreads();
   };
 
-  // The pieces of this workgroup.  Plain launch: one workgroup per block (XCD-aware
-  // numbering: hardware deals block ids round-robin over the XCDs; each XCD gets a
-  // contiguous range of blocks, so query tiles of one head share its L2 while they
-  // stream the same keys).  Split launch: one workgroup per CU; on each XCD workgroup
-  // i < nb walks the first J - t tiles of its block (in step with the others, as
-  // above) and the ns = per_xcd - nb spare workgroups share the blocks' last t tiles
-  // ("tails"), so every CU gets about the same number of tiles.
-  const int J = ntiles;
-  if (!sp.on || int(blockIdx.x) / NXCD < XcdPlan(sp, blockIdx.x % NXCD).nb) {
-    int blk, jb = J, npc = 1;
-    if (!sp.on) {
-      const int per_xcd = (sp.B + NXCD - 1) / NXCD;
-      blk = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-      if (blk >= sp.B) return;
-    } else {
-      const XcdPlan xp(sp, blockIdx.x % NXCD);
-      const int i = blockIdx.x / NXCD;
-      blk = xp.b0 + i;
-      jb = J - xp.t;
-      npc = xp.t ? 1 + xp.n_tail(i) : 1;
-    }
-    piece(blk, 0, jb, npc, blk);
-    return;
-  }
-  const XcdPlan xp(sp, blockIdx.x % NXCD);
-  const int sidx = int(blockIdx.x) / NXCD - xp.nb;
-  if (sidx >= xp.ns || xp.t == 0) return;
-  const int u1 = min((sidx + 1) * xp.L, xp.nb * xp.t);
-  for (int u = sidx * xp.L; u < u1;) {
-    const int bl = u / xp.t;
-    const int e = min(u1, (bl + 1) * xp.t);
-    const int blk = xp.b0 + bl;
-    const int ja = J - xp.t + (u - bl * xp.t);
-    piece(blk, ja, ja + (e - u), 1 + xp.n_tail(bl), sp.B + 2 * blk + (xp.first_spare(bl) == sidx ? 0 : 1));
-    u = e;
-  }
+  // The pieces of this workgroup (split_plan.h): one block per workgroup, or with the
+  // split walk a head piece or a spare's run of tail pieces.
+  for_each_piece(sp, int(blockIdx.x), piece);
 }
 
 
 template <int D, int NQB, int NW, int KVQ, int MINB = 1>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const int rows = NW * 32 * NQB;
+  static_assert(NW * 32 * NQB <= kAttnRows, "work-area slot size");
   Split sp{};
   sp.n_qtiles = (p.nq + rows - 1) / rows;
   sp.B = sp.n_qtiles * p.H;
@@ -947,19 +884,8 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   for (int k = 0; k < p.nrun; ++k) sp.J += (p.run_rows[k] + BN - 1) / BN;
   sp.ws = p.ws;
   sp.cnt = p.cnt;
-  // Split when the blocks leave CUs idle, every XCD has at least as many blocks as spare
-  // workgroups (so L >= t) and the walk is long enough to be worth a merge.
-  bool on = p.ws && p.cnt && p.n_cu % NXCD == 0 && sp.B < p.n_cu && sp.J >= 32 &&
-            split_slot_floats(D, rows) * 3 * int64_t(p.n_cu) <= p.ws_floats;
-  if (on) {
-    sp.per_xcd = p.n_cu / NXCD;
-    for (int x = 0; x < NXCD && on; ++x) {
-      const XcdPlan xp(sp, x);
-      on = xp.nb >= 1 && xp.nb >= xp.ns && (xp.t == 0 || xp.L >= xp.t);
-    }
-  }
-  sp.on = on;
-  const int grid = on ? p.n_cu : (sp.B + NXCD - 1) / NXCD * NXCD;
+  const bool on = plan_split(sp, p.n_cu, p.ws_slots);
+  const int grid = on ? p.n_cu : (sp.B + kXcds - 1) / kXcds * kXcds;
   if (p.nrun > 1)
     hipLaunchKernelGGL((attn_kernel<D, NQB, NW, MINB, KVQ, true>), dim3(grid), dim3(64 * NW), 0, s, p, sp);
   else

@@ -1,7 +1,8 @@
 // cache.cpp -- the C ABI: cache handle, host bookkeeping, validation, kernel dispatch.
 //
 // The handle owns one device allocation holding, per layer, the K and V slot arrays
-// [S+W][T][H][D] (bf16 or int8) and, for int8, their [S+W][T][H] fp32 scales.  Host
+// [S+W][T][H][D] (bf16, int8 or fp8), for int8 / fp8 their [S+W][T][H] fp32 scales,
+// and the attention work area of the split key walk (partials and counters).  Host
 // bookkeeping per layer: frames seen (f0) and the frame held by each slot.  Every
 // argument is checked before the first HIP call so that errors are testable on a
 // machine without a GPU.
@@ -32,8 +33,14 @@ struct ll_cache {
   size_t kv_bytes = 0;          // one K (or V) slot array of one layer
   size_t sc_bytes = 0;          // one K (or V) scale array of one layer
   int n_cu = 0;                 // compute units of the device
-  size_t ws_offset = 0;         // attention work-split buffers: partial results, then counters
-  int64_t ws_floats = 0;
+  // Attention work-split buffers, one set per layer (layers may run on different
+  // streams at once): partial-result slots, then after all layers' slots the per-block
+  // arrival counters.
+  size_t ws_offset = 0;
+  size_t ws_layer_bytes = 0;
+  int64_t ws_slots = 0;
+  size_t cnt_offset = 0;
+  size_t cnt_layer_bytes = 0;
   void* mem = nullptr;
   std::vector<int64_t> f0;
   std::vector<int64_t> fs;      // first frame of the current shot (shot sink)
@@ -51,8 +58,8 @@ struct ll_cache {
     return sc_bytes ? reinterpret_cast<float*>(base() + size_t(2) * layers * kv_bytes + (size_t(2) * l + 1) * sc_bytes)
                     : nullptr;
   }
-  float* ws() const { return reinterpret_cast<float*>(base() + ws_offset); }
-  int* cnt() const { return reinterpret_cast<int*>(base() + ws_offset + size_t(ws_floats) * 4); }
+  float* ws(int l) const { return reinterpret_cast<float*>(base() + ws_offset + size_t(l) * ws_layer_bytes); }
+  int* cnt(int l) const { return reinterpret_cast<int*>(base() + cnt_offset + size_t(l) * cnt_layer_bytes); }
 };
 
 namespace {
@@ -180,19 +187,31 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
   int n_cu = 0;
   e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  // Work-split buffers of the attention launch (partial results of at most three pieces
-  // per block, blocks < CUs; one arrival counter per CU), after the cache arrays.
-  const int64_t ws_floats = ll::split_ws_floats(head_dim, n_cu);
+  // Work-split buffers of the attention launches, per layer: partial-result slots (fewer
+  // than two per CU, split_plan.h) and one arrival counter per block (blocks < CUs when
+  // the walk is split), after the cache arrays.
+  const int64_t ws_slots = ll::split_slots(n_cu);
+  const int64_t ws_layer_bytes = round256(ll::split_slot_floats(head_dim, ll::kAttnRows) * ws_slots * 4);
+  const int64_t cnt_layer_bytes = round256(int64_t(n_cu) * 4);
   const int64_t ws_offset = int64_t(cache_total);
-  const double total = cache_total + double(ws_floats) * 4 + double(round256(int64_t(n_cu) * 4));
+  const int64_t cnt_offset = ws_offset + int64_t(layers) * ws_layer_bytes;
+  const double total = double(cnt_offset) + double(layers) * double(cnt_layer_bytes);
   void* mem = nullptr;
   e = hipMalloc(&mem, size_t(total));
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(LL_ERR_OOM, "hipMalloc of %.3g bytes failed: %s", total, hipGetErrorString(e));
   }
-  e = hipMemset(static_cast<char*>(mem) + ws_offset + ws_floats * 4, 0, size_t(n_cu) * 4);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  // Zero the counters on a private stream and wait for that stream only.
+  hipStream_t zs = nullptr;
+  e = hipStreamCreateWithFlags(&zs, hipStreamNonBlocking);
+  if (e == hipSuccess) {
+    e = hipMemsetAsync(static_cast<char*>(mem) + cnt_offset, 0, size_t(layers) * size_t(cnt_layer_bytes), zs);
+    const hipError_t e2 = hipStreamSynchronize(zs);
+    if (e == hipSuccess) e = e2;
+    const hipError_t e3 = hipStreamDestroy(zs);
+    if (e == hipSuccess) e = e3;
+  }
   if (e != hipSuccess) {
     (void)hipFree(mem);
     return hip_fail(e, "clearing the work-split counters");
@@ -212,7 +231,10 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
   c->sc_bytes = size_t(sc_bytes);
   c->n_cu = n_cu;
   c->ws_offset = size_t(ws_offset);
-  c->ws_floats = ws_floats;
+  c->ws_layer_bytes = size_t(ws_layer_bytes);
+  c->ws_slots = ws_slots;
+  c->cnt_offset = size_t(cnt_offset);
+  c->cnt_layer_bytes = size_t(cnt_layer_bytes);
   c->mem = mem;
   c->f0.assign(size_t(layers), 0);
   c->fs.assign(size_t(layers), 0);
@@ -271,9 +293,9 @@ ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void*
   }
   p.H = c->heads;
   p.c = float(1.4426950408889634 / std::sqrt(double(c->head_dim)));
-  p.ws = c->ws();
-  p.ws_floats = c->ws_floats;
-  p.cnt = c->cnt();
+  p.ws = c->ws(layer);
+  p.ws_slots = c->ws_slots;
+  p.cnt = c->cnt(layer);
   p.n_cu = c->n_cu;
   hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");

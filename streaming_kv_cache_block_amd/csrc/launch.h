@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "split_plan.h"
+
 namespace ll {
 
 constexpr int kMaxPlan = 128;  // = LL_MAX_SLOTS
@@ -27,10 +29,11 @@ struct AttnParams {
   int run_rows[kMaxRuns];
   int H;
   float c;              // log2(e) / sqrt(D)
-  // Work-split buffers (owned by the cache; may be null: then no split): partial
-  // results and per-block arrival counters (all zero between calls), CU count.
+  // Work-split buffers of this call (the layer's own, so layers may run concurrently
+  // on different streams; may be null: then no split): partial-result slots, per-block
+  // arrival counters (all zero between calls), CU count.
   float* ws;
-  int64_t ws_floats;
+  int64_t ws_slots;
   int* cnt;
   int n_cu;
 };
@@ -40,19 +43,8 @@ inline __host__ __device__ int64_t split_slot_floats(int D, int rows) {
   return (int64_t(rows) * (D + 2) + 63) / 64 * 64;
 }
 
-// Work description of one attention launch (device side: attn.hip).
-struct Split {
-  int B;          // blocks = heads x query tiles
-  int n_qtiles;
-  int J;          // key tiles per block
-  int on;         // 1: one workgroup per CU, tails of the key walk shared (per XCD)
-  int per_xcd;    // workgroups per XCD when on
-  float* ws;
-  int* cnt;
-};
-
-// Partial-result slots a split launch may use: blocks < CUs, three pieces at most.
-inline int64_t split_ws_floats(int D, int n_cu) { return split_slot_floats(D, 256) * 3 * int64_t(n_cu); }
+// Most query rows of one attention block (the work area's slot size is for these).
+constexpr int kAttnRows = 256;
 
 // kv_fmt: 0 bf16 cache, 1 int8 codes, 2 fp8 (E4M3) codes (+ fp32 scales).
 hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t s);

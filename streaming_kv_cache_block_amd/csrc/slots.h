@@ -19,12 +19,27 @@
 // scanned in physical order (softmax attention does not depend on key order).
 // Without a shot sink the occupied slots are exactly the prefix [0, min(f0, S + W)).
 //
-// Builds with plain g++ (no HIP) for host-only tests.
+// Builds with plain g++ (no HIP) for host-only tests.  With LL_DEBUG defined every
+// slot index and plan entry is bounds-checked (abort with a message on failure).
 #pragma once
 
 #include <algorithm>
 #include <cstdint>
 #include <vector>
+
+#ifdef LL_DEBUG
+#include <cstdio>
+#include <cstdlib>
+#define LL_CHECK(cond)                                                                      \
+  do {                                                                                      \
+    if (!(cond)) {                                                                          \
+      std::fprintf(stderr, "LL_DEBUG check failed: %s (%s:%d)\n", #cond, __FILE__, __LINE__); \
+      std::abort();                                                                         \
+    }                                                                                       \
+  } while (0)
+#else
+#define LL_CHECK(cond) ((void)0)
+#endif
 
 namespace ll {
 
@@ -50,6 +65,7 @@ inline int slots_of(int64_t f, const Layout& L, int64_t fs, int out[2]) {
   int n = 0;
   if (f >= fs && f < fs + L.Ss) out[n++] = L.S + int(f - fs);
   if (L.W > 0) out[n++] = L.S + L.Ss + int((f - L.S) % L.W);
+  for (int j = 0; j < n; ++j) LL_CHECK(out[j] >= L.S && out[j] < L.slots());
   return n;
 }
 
@@ -108,6 +124,8 @@ inline std::vector<SlotRun> cache_runs(int64_t f0, const Layout& L, int64_t fs) 
   const int64_t lo = std::max<int64_t>(L.S, fs), hi = std::min<int64_t>({fs + L.Ss, f0, wlo});
   if (hi > lo) add(L.S + int(lo - fs), int(hi - lo));
   add(L.S + L.Ss, int(std::max<int64_t>(0, f0 - wlo)));
+  LL_CHECK(runs.size() <= 3);
+  for (const SlotRun& r : runs) LL_CHECK(r.first >= 0 && r.count > 0 && r.first + r.count <= L.slots());
   return runs;
 }
 
@@ -123,6 +141,7 @@ inline std::vector<WriteEntry> append_plan(int64_t f0, int n, const Layout& L, i
   std::vector<WriteEntry> out;
   for (int s = 0; s < L.slots(); ++s)
     if (last[size_t(s)] >= 0) out.push_back({last[size_t(s)], s, f0 + last[size_t(s)]});
+  for (const WriteEntry& e : out) LL_CHECK(e.src >= 0 && e.src < n && e.slot >= 0 && e.slot < L.slots());
   return out;
 }
 inline std::vector<WriteEntry> append_plan(int64_t f0, int n, int S, int W) {
@@ -138,7 +157,9 @@ inline std::vector<WriteEntry> recache_plan(int64_t f0, const Layout& L, int64_t
     int s[2];
     const int k = held_slots(fr[i], f0, L, fs, s);
     for (int j = 0; j < k; ++j) out.push_back({int(i), s[j], fr[i]});
+    LL_CHECK(k >= 1);   // every retained frame is held somewhere
   }
+  LL_CHECK(int64_t(out.size()) <= L.slots());
   return out;
 }
 inline std::vector<WriteEntry> recache_plan(int64_t f0, int S, int W) { return recache_plan(f0, Layout{S, 0, W}, 0); }

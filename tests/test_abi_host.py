@@ -121,7 +121,9 @@ def _check_cli_against_model(lines, expect):
         # the slot runs cover exactly the slots holding the retained frames, each frame once
         run_frames = [slot_frame[s] for first, count in g["runs"] for s in range(first, first + count)]
         assert sorted(run_frames) == retained
-        assert run_frames == sorted(run_frames) or Ss == 0 or True
+        # runs are in ascending slot order, disjoint and not adjacent (adjacent runs merge)
+        for (a0, an), (b0, _) in zip(g["runs"], g["runs"][1:]):
+            assert a0 + an < b0, g["runs"]
         assert len(g["runs"]) <= 3
         # recache: block idx -> the idx-th retained frame, in every slot the model holds it in
         blocks = {}
@@ -174,3 +176,86 @@ def test_slot_math_with_shot_sinks_matches_oracle_ring_model():
                         window = list(range(max(S, r.f0 - W), r.f0))
                         expect.append((S, Ss, W, r.f0, r.fs, list(r.slot_frame), r.retained_frames(), window))
     _check_cli_against_model(lines, expect)
+
+
+def _check_split_plan(rec):
+    B, J, n_cu = rec["B"], rec["J"], rec["n_cu"]
+    by_blk = {}
+    for wg, blk, ja, jb, npc, slot, tail0 in rec["pieces"]:
+        assert 0 <= wg < (n_cu if rec["on"] else (B + 7) // 8 * 8)
+        assert 0 <= blk < B and 0 <= ja < jb <= J
+        by_blk.setdefault(blk, []).append((ja, jb, npc, slot, tail0))
+    assert sorted(by_blk) == list(range(B)), "every block runs"
+    used = set()
+    for blk, ps in by_blk.items():
+        ps.sort()
+        # the pieces tile the block's key walk [0, J) exactly once
+        assert ps[0][0] == 0 and ps[-1][1] == J
+        assert all(a[1] == b[0] for a, b in zip(ps, ps[1:]))
+        assert all(p[2] == len(ps) for p in ps) and len(ps) <= 3
+        if len(ps) == 1:
+            continue
+        assert rec["on"]
+        assert ps[0][3] == blk                                    # head piece: the block's own slot
+        t0 = {p[4] for p in ps}
+        assert len(t0) == 1
+        tails = [p[3] for p in ps[1:]]
+        assert tails == [ps[0][4] + k for k in range(len(tails))]  # tail slots tail0, tail0 + 1
+        for s in [blk] + tails:
+            assert 0 <= s < rec["slots"] and s not in used, (blk, s)
+            used.add(s)
+
+
+def test_split_walk_plan_covers_every_key_once_with_unique_slots():
+    """The split attention launch's plan (split_plan.h, g++ build): each block's key
+    tiles are walked exactly once across its pieces, at most three pieces per block,
+    and every partial result has its own slot below the work area's 2 x CUs."""
+    lines = []
+    for n_cu in (256, 304, 80, 8):
+        for B in (1, 7, 8, 9, 24, 100, 152, 156, 168, 200, 208, 228, 255, 256, 300):
+            for J in (1, 31, 32, 33, 64, 100, 440, 659, 2000):
+                lines.append(f"split {B} {J} {n_cu}")
+    recs = _run_cli(lines)
+    assert len(recs) == len(lines)
+    n_on = 0
+    for rec in recs:
+        _check_split_plan(rec)
+        n_on += rec["on"]
+        if rec["B"] == 228 and rec["J"] == 440 and rec["n_cu"] == 256:
+            assert rec["on"] == 1     # the steady shape takes the split walk
+    assert n_on > 50
+
+
+class _FakeTensor:
+    """Stands in for a device tensor in the binding's argument checks (no GPU here):
+    shape and element count only; the checks must fire before any pointer is taken."""
+
+    def __init__(self, *shape):
+        self.shape = shape
+
+    def numel(self):
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+
+def test_binding_rejects_mis_shaped_tensors_before_the_library():
+    c = ll.Cache.__new__(ll.Cache)          # a handle-less object: only the checks run
+    c.layers, c.heads, c.head_dim, c.T, c.S, c.W, c.Ss = 1, 12, 128, 1560, 3, 12, 0
+    good = _FakeTensor(3 * 1560, 12, 128)
+    for bad in (_FakeTensor(3 * 1560, 12, 64), _FakeTensor(3 * 1560, 8, 128), _FakeTensor(2 * 1560 + 1, 12, 128)):
+        with pytest.raises(ValueError):
+            c.attn(0, good, good, bad, out=good)
+        with pytest.raises(ValueError):
+            c.attn(0, good, good, good, out=bad)
+        with pytest.raises(ValueError):
+            c.append(0, good, bad)
+        with pytest.raises(ValueError):
+            c.recache(0, good, bad)
+    with pytest.raises(ValueError):           # explicit n_frames larger than the tensors
+        c.attn(0, good, good, good, out=good, n_frames=4)
+    with pytest.raises(ValueError):
+        c.recache_from_hidden(0, _FakeTensor(15 * 1560, 1536), _FakeTensor(1536, 1536), _FakeTensor(1536, 1024))
+    with pytest.raises(ValueError):
+        ll.kv_project(_FakeTensor(100, 1536), _FakeTensor(1536, 1536), _FakeTensor(1536, 1535))

@@ -139,7 +139,8 @@ def _rollout(torch, cfg, layers, check_layers, check_chunks, slot_chunks):
                     qb, kb, vb = synth.to_bits(q), synth.to_bits(kc), synth.to_bits(vc)
                     ref = attention.chunk_attention(qb, kb, vb, hist[l], hist[l].f0, S, W, T,
                                                     kv_int8=cfg.kv_int8, rows=rows)
-                    mx, _ = compare_attention(synth.to_bits(out)[rows], ref, f"layer {l} chunk {k} pass {p}")
+                    mx, _ = compare_attention(synth.to_bits(out)[rows], ref, f"layer {l} chunk {k} pass {p}",
+                                              scale_gate=True)
                     worst = max(worst, mx)
                     n_checks += 1
                 if p == cfg.passes - 1:

@@ -62,10 +62,10 @@ def test_steady_state_step(torch_gpu, kv):
         t0 = time.time()
         if p == 0:
             ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv)
-            mx, mn = compare_attention(out, ref, f"pass {p} (all rows)")
+            mx, mn = compare_attention(out, ref, f"pass {p} (all rows)", scale_gate=True)
         else:
             ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv, rows=rows)
-            mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"pass {p} (sampled rows)")
+            mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"pass {p} (sampled rows)", scale_gate=True)
         _log(f"steady kv={kv} pass {p}: max-abs {mx:.2e} mean-abs {mn:.2e} oracle {time.time() - t0:.1f}s")
     cache.append(0, synth.to_device(kc), synth.to_device(vc))
     hist.append(kc, vc)
@@ -146,7 +146,7 @@ def test_recache_projection_then_rewrite_then_attention(torch_gpu):
     out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
     rows = sample_rows(cfg.nq, T, seed=3)
     ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, rows=rows)
-    compare_attention(synth.to_bits(out)[rows], ref, "attention after recache")
+    compare_attention(synth.to_bits(out)[rows], ref, "attention after recache", scale_gate=True)
 
 
 def test_frame_id_probe_at_full_shape(torch_gpu):
@@ -207,7 +207,7 @@ def test_attention_split_walk_shapes(torch_gpu, H, C, D, kv):
         rows |= {t0, min(t0 + tile_rows, nq) - 1}
     rows = sorted(rows)
     ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv=kv, rows=rows)
-    mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"H={H} C={C} D={D} kv={kv}")
+    mx, mn = compare_attention(synth.to_bits(out)[rows], ref, f"H={H} C={C} D={D} kv={kv}", scale_gate=True)
     _log(f"split walk H={H} C={C} D={D} kv={kv}: {len(rows)} rows, max-abs {mx:.2e} mean-abs {mn:.2e}")
     # the same chunk again: the arrival counters were reset by the merges
     out2 = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))

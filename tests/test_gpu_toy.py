@@ -161,21 +161,33 @@ def test_recache_overwrites_every_slot(torch_gpu, kv):
     assert e.value.status == ll.LL_ERR_STATE
 
 
-def test_recache_window_keeps_sink(torch_gpu):
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_recache_window_keeps_sink(torch_gpu, kv):
+    """Window-only recache (techwalker.com article, §六): the window frames' slots get the
+    new blocks (oracle.ring's window order), the sink keeps its bytes, and the next
+    chunk's attention sees the new window and the old sink."""
     T, H, D, S, W, C = 16, 2, 64, 3, 6, 3
-    cache = ll.Cache(1, H, D, T, S, W)
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     hist = History(S, W, T)
     for k in range(4):
         kb = synth.normal_bf16((C * T, H, D), 1.0, 93, k, 0)
         vb = synth.normal_bf16((C * T, H, D), 1.0, 93, k, 1)
         cache.append(0, synth.to_device(kb), synth.to_device(vb))
         hist.append(kb, vb)
-    n = min(max(hist.f0 - S, 0), W)
+    n = len(hist.model.window_frames())
     K_w = synth.normal_bf16((n * T, H, D), 1.0, 94, 0)
     V_w = synth.normal_bf16((n * T, H, D), 1.0, 94, 1)
     cache.recache_window(0, synth.to_device(K_w), synth.to_device(V_w))
     hist.recache_window(K_w, V_w)
-    check_slots(cache, 0, hist)
+    check_slots(cache, 0, hist, kv=kv)
+    for p in range(2):
+        q, kc, vc = (synth.normal_bf16((C * T, H, D), 1.0, 95, p, t) for t in range(3))
+        out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+        ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv=kv)
+        compare_attention(out, ref, f"after window recache, pass {p}")
+    with pytest.raises(ll.LLError) as e:
+        cache.recache_window(0, synth.to_device(K_w[:T]), synth.to_device(V_w[:T]))
+    assert e.value.status == ll.LL_ERR_STATE
 
 
 def test_empty_cache_first_chunk_and_ragged_lengths(torch_gpu):

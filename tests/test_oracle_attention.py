@@ -164,3 +164,113 @@ def test_gathered_keys_equal_explicit_minus_inf_mask():
         for h in range(H):
             ref = attention.masked_attention(q[:, h], Kall[:, h], Vall[:, h], m, attention.softmax_scale(D))
             np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=2e-6)
+
+
+# ---- low-bit caches (LongLive-2.0 explainer, wmrh.cn, §15.2-§15.3: the history
+# cache is kept in low precision and dequantised where it is used; the own chunk
+# is the chunk being computed and is used as given) ----------------------------
+
+def _exact_history(kind, n_frames, T, H, D, seed):
+    """History frames whose per-row quantisation is exact: int8 rows are integers in
+    [-127, 127] with one entry at +-127 (scale 127/127 = 1, codes = values); fp8 rows
+    are E4M3 values with one entry at +-448 (scale 448/448 = 1)."""
+    from oracle import quant
+    rng = np.random.default_rng(seed)
+    if kind == "int8":
+        x = rng.integers(-127, 128, size=(n_frames * T, H, D)).astype(np.float32)
+        top = 127.0
+    else:
+        vals = quant.e4m3_values()
+        x = (vals[rng.integers(0, 127, size=(n_frames * T, H, D))] *
+             rng.choice([-1.0, 1.0], size=(n_frames * T, H, D))).astype(np.float32)
+        top = 448.0
+    col = rng.integers(0, D, size=(n_frames * T, H))
+    np.put_along_axis(x, col[..., None], (top * rng.choice([-1.0, 1.0], size=(n_frames * T, H)))[..., None]
+                      .astype(np.float32), axis=-1)
+    bits = bf16.round_f32(x)
+    assert (bf16.to_f32(bits) == x).all()          # every such value is a bf16 value
+    return bits
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_low_bit_attention_equals_bf16_when_quantisation_is_exact(kind):
+    """History rows that quantise exactly make the low-bit oracle equal the bf16 one bit
+    for bit, while the own chunk is generic Gaussian data that would NOT survive
+    quantisation: so equality also shows the own chunk is used as given."""
+    C, T, H, D, S, W = 3, 16, 2, 64, 3, 6
+    n_hist = 12
+    kh = _exact_history(kind, n_hist, T, H, D, seed=31)
+    vh = _exact_history(kind, n_hist, T, H, D, seed=32)
+    hist = lambda f: (kh[f * T:(f + 1) * T], vh[f * T:(f + 1) * T])
+    from oracle import quant
+    for f0 in (0, 3, 9, 12):
+        q, kc, vc = (synth.normal_bf16((C * T, H, D), 1.0, 33, f0, t) for t in range(3))
+        # the own chunk really is changed by quantisation (else the check proves nothing)
+        deq = quant.dequantize(*quant.quantize(bf16.to_f32(kc))) if kind == "int8" else \
+            quant.dequantize_fp8(*quant.quantize_fp8(bf16.to_f32(kc)))
+        assert (deq != bf16.to_f32(kc)).any()
+        a = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kind)
+        b = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv="bf16")
+        assert np.array_equal(a, b), (kind, f0)
+
+
+def _worked_case(kind):
+    """One sink frame, one window frame and a one-frame own chunk, one token per frame,
+    one head of 4 dims (scale 1/sqrt(4) = 1/2).  Every history row has its absmax
+    (127 or 448) in a dim the query ignores, so the scale is exactly 1 and each other
+    entry is rounded by hand to the format's nearest value, ties to even:
+      int8: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -3.5 -> -4
+      fp8 (E4M3, 3 mantissa bits): 1.0625 -> 1, 1.1875 -> 1.25, 3.125 -> 3, -5.25 -> -5
+    Returns (history K, V rows given, the same rows as the format represents them,
+    own K, own V, query)."""
+    if kind == "int8":
+        M, a, b, c, d = 127.0, (0.5, 0.0), (1.5, 2.0), (2.5, 2.0), (-3.5, -4.0)
+    else:
+        M, a, b, c, d = 448.0, (1.0625, 1.0), (1.1875, 1.25), (3.125, 3.0), (-5.25, -5.0)
+    K_in = [[a[0], 0, M, 0], [b[0], 0, -M, 0]]
+    K_hat = [[a[1], 0, M, 0], [b[1], 0, -M, 0]]
+    V_in = [[c[0], M, 0, 0], [d[0], 0, M, 0]]
+    V_hat = [[c[1], M, 0, 0], [d[1], 0, M, 0]]
+    own_k = [[1.0, 0.0, 0.0, 0.3]]
+    own_v = [[0.5, 0.25, -0.75, 1.0]]   # absmax 1: int8 / fp8 would change 0.5 and 0.25 / 0.3
+    q = [[2.0, 0.0, 0.0, 0.0]]
+    return K_in, V_in, K_hat, V_hat, own_k, own_v, q
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_low_bit_attention_worked_example(kind):
+    """Closed form of the worked case: scores q.k/2 over the dequantised sink and window
+    keys and the own key as given, softmax, weighted sum of the dequantised history
+    values and the own value as given.  Leaving K or V unquantised, or quantising the
+    own chunk, changes the result by far more than the tolerance."""
+    import math
+    K_in, V_in, K_hat, V_hat, own_k, own_v, q = _worked_case(kind)
+    as_bits = lambda rows: bf16.round_f32(np.array(rows, dtype=np.float32).reshape(len(rows), 1, 4))
+    kh, vh = as_bits(K_in), as_bits(V_in)
+    hist = lambda f: (kh[f:f + 1], vh[f:f + 1])
+    got = attention.chunk_attention(as_bits(q), as_bits(own_k), as_bits(own_v), hist, 2, 1, 1, 1,
+                                    kv=kind, dtype=np.float64)[0, 0]
+
+    def closed_form(keys, vals):
+        s = [sum(qi * ki for qi, ki in zip(q[0], k)) / 2.0 for k in keys]
+        e = [math.exp(x - max(s)) for x in s]
+        return np.array([sum(e[j] * vals[j][d] for j in range(3)) / sum(e) for d in range(4)])
+
+    want = closed_form(K_hat + own_k, V_hat + own_v)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # Planted readings, each worked out the same way by hand: history K as given, history
+    # V as given, and the own chunk passed through the format (its rows have absmax 1,
+    # so the scale is 1/M and each entry becomes rint(x M) / M or E4M3(x M) / M).
+    M = 127.0 if kind == "int8" else 448.0
+    if kind == "int8":
+        own_q = lambda row: [float(np.rint(x * M)) / M for x in row]
+    else:
+        from oracle import quant
+        own_q = lambda row: [float(quant.e4m3_to_f32(quant.round_e4m3(np.float32(x * M)))) / M for x in row]
+    planted = {
+        "K unquantised": closed_form(K_in + own_k, V_hat + own_v),
+        "V unquantised": closed_form(K_hat + own_k, V_in + own_v),
+        "own chunk quantised": closed_form(K_hat + [own_q(own_k[0])], V_hat + [own_q(own_v[0])]),
+    }
+    for name, alt in planted.items():   # each is far outside the pin's 1e-12 tolerance
+        assert np.abs(alt - want).max() > 1e-4, name

@@ -20,7 +20,7 @@ def test_bf16_rounding_matches_torch_including_ties():
     # exact ties: upper half odd/even with lower half 0x8000
     ties = (np.arange(0, 4096, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
     ties = ties[np.isfinite(ties)]
-    for arr in (x, ties, np.array([0.0, -0.0, 1e-40, -3.5e38], dtype=np.float32)):
+    for arr in (x, ties, np.array([0.0, -0.0, 1e-40, -3.3e38, 3.39e38, -np.inf], dtype=np.float32)):
         assert (bf16.round_f32(arr) == _torch_bf16_bits(arr)).all()
     bits = synth.normal_bf16((1000,), 1.0, 5)
     assert (bf16.round_f32(bf16.to_f32(bits)) == bits).all()   # exact round trip

@@ -172,3 +172,68 @@ def test_ring_model_with_shots_holds_exactly_the_cached_visible_frames():
                         for s, f in enumerate(r.slot_frame):
                             if f >= 0:
                                 assert s in r.slots_of(f)
+
+
+def _fifo_window(f0, S, W):
+    """The non-sink frames a FIFO of capacity W holds after frames 0 .. f0-1 arrive
+    one at a time (sink frames never enter it), oldest first."""
+    fifo = deque()
+    for f in range(f0):
+        if f >= S:
+            fifo.append(f)
+            while len(fifo) > W:
+                fifo.popleft()
+    return list(fifo)
+
+
+@pytest.mark.parametrize("S", [0, 1, 3])
+@pytest.mark.parametrize("W", [1, 2, 5, 12, 21])
+@pytest.mark.parametrize("n", [1, 3, 4, 13])
+def test_window_recache_rewrites_only_the_window(S, W, n):
+    """techwalker.com article, §六: the narrower recache recomputes only the recent
+    window and leaves the sink as it was.  Its frame list must equal a FIFO replay of
+    the non-sink frames; sink slots keep their bytes, every window slot gets the block
+    of its frame's position in that list."""
+    r = ring.RingModel(S, W)
+    for step in range(12):
+        r.append(n, src_of_frame=lambda f: ("append", f))
+        win = r.window_frames()
+        assert win == _fifo_window(r.f0, S, W)
+        assert win == [f for f in visibility.cached_visible_frames(r.f0, S, W) if f >= S]
+        if not win:
+            with pytest.raises(ValueError):
+                r.recache_window(0)
+            continue
+        before = list(r.slot_src)
+        r.recache_window(len(win), src_of_block=lambda idx: ("window", step, idx))
+        for s, f in enumerate(r.slot_frame):
+            if f < 0:
+                continue
+            if f < S:
+                assert r.slot_src[s] == before[s] == ("append", f)
+            else:
+                assert r.slot_src[s] == ("window", step, win.index(f))
+        with pytest.raises(ValueError):
+            r.recache_window(len(win) + 1)
+        # restore the appended bytes' tags so the next step's sink check stays exact
+        for s, f in enumerate(r.slot_frame):
+            if f >= 0:
+                r.slot_src[s] = ("append", f)
+
+
+def test_window_recache_with_shot_sink_keeps_shot_frames_outside_window():
+    """With a shot sink, a shot-sink frame that has left the window is not part of the
+    window recache; one still in the window is rewritten in both of its slots."""
+    S, Ss, W = 1, 2, 3
+    r = ring.RingModel(S, W, Ss)
+    r.append(4, src_of_frame=lambda f: ("append", f))
+    r.begin_shot()                          # shot starts at frame 4
+    r.append(6, src_of_frame=lambda f: ("append", f))   # frames 4..9; window = 7, 8, 9
+    assert r.window_frames() == [7, 8, 9]
+    r.recache_window(3, src_of_block=lambda idx: ("window", idx))
+    for s, f in enumerate(r.slot_frame):
+        if f in (7, 8, 9):
+            assert r.slot_src[s] == ("window", f - 7)
+        elif f >= 0:
+            assert r.slot_src[s] == ("append", f), (s, f)
+    assert sorted(f for f in r.slot_frame if f >= 0) == [0, 4, 5, 7, 8, 9]
