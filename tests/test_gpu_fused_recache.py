@@ -117,8 +117,9 @@ def test_fused_recache_argument_errors(torch_gpu):
         cache.recache_from_hidden(0, h[:16], w, w)
     assert e.value.status == ll.LL_ERR_STATE
     h96 = torch.zeros((3 * 16, 96), device="cuda", dtype=torch.bfloat16)
-    with pytest.raises(ll.LLError) as e:        # d_in not a multiple of 64
-        cache.recache_from_hidden(0, h96, w, w)
+    w96 = torch.zeros((128, 96), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(ll.LLError) as e:        # d_in not a multiple of 64 (the library's check)
+        cache.recache_from_hidden(0, h96, w96, w96)
     assert e.value.status == ll.LL_ERR_INVALID
     odd = ll.Cache(1, 1, 64, 16, 3, 6)          # heads*head_dim = 64
     odd.append(0, torch.zeros((16, 1, 64), device="cuda", dtype=torch.bfloat16),
@@ -126,3 +127,5 @@ def test_fused_recache_argument_errors(torch_gpu):
     with pytest.raises(ll.LLError) as e:
         odd.recache_from_hidden(0, h[:16], w[:64], w[:64])
     assert e.value.status == ll.LL_ERR_INVALID
+    with pytest.raises(ValueError):             # weights that do not match h: the binding's check
+        cache.recache_from_hidden(0, h, w[:, :64], w[:, :64])
