@@ -88,17 +88,28 @@ struct Piece {
 template <class F>
 LL_HD void for_each_piece(const Split& sp, int wg, F&& f) {
   const int J = sp.J;
+  // one call site for the block-sized piece (no split, or a head piece), one for the
+  // tails: the piece body is large and inlined at each
+  Piece whole{-1, 0, J, 1, 0, 0};
+  XcdPlan xp;
+  int i = 0;
   if (!sp.on) {
     const int per_xcd = (sp.B + kXcds - 1) / kXcds;
-    const int blk = (wg % kXcds) * per_xcd + wg / kXcds;
-    if (blk < sp.B) f(Piece{blk, 0, J, 1, blk, 0});
-    return;
+    whole.blk = (wg % kXcds) * per_xcd + wg / kXcds;
+    whole.slot = whole.blk;
+    if (whole.blk >= sp.B) whole.blk = -1;
+  } else {
+    xp = XcdPlan(sp, wg % kXcds);
+    i = wg / kXcds;
+    if (i < xp.nb) {
+      whole.blk = whole.slot = xp.b0 + i;
+      whole.jb = J - xp.t;
+      whole.npc = xp.t ? 1 + xp.n_tail(i) : 1;
+      whole.tail0 = xp.t ? xp.tail_base(i) : 0;
+    }
   }
-  const XcdPlan xp(sp, wg % kXcds);
-  const int i = wg / kXcds;
-  if (i < xp.nb) {
-    const int npc = xp.t ? 1 + xp.n_tail(i) : 1;
-    f(Piece{xp.b0 + i, 0, J - xp.t, npc, xp.b0 + i, xp.t ? xp.tail_base(i) : 0});
+  if (!sp.on || i < xp.nb) {
+    if (whole.blk >= 0) f(whole);
     return;
   }
   const int sidx = i - xp.nb;
