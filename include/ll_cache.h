@@ -91,7 +91,10 @@ typedef enum {
  * an attention work area for split key walks (2 * CUs partial results of 256 rows *
  * (head_dim + 2) * 4 bytes and CUs arrival counters: about 68 MB for head_dim 128 on
  * 256 CUs).  Slot contents start undefined; no slot is visible until written.  The
- * call waits only for the zeroing of its own counters (a private stream).
+ * first cache on a device also sets up the static scratch of
+ * ll_attn_sink_window_noalloc there (LL_NOALLOC_SCRATCH_BYTES, held by the loaded
+ * library until the process ends).  The call waits only for its own zeroing work (a
+ * private stream).
  * Errors: LL_ERR_INVALID, LL_ERR_OOM, LL_ERR_HIP.
  */
 ll_status ll_cache_create(int layers, int heads, int head_dim, int tokens_per_frame,
@@ -165,6 +168,27 @@ ll_status ll_cache_append(ll_cache *c, int layer, const void *K, const void *V,
  */
 ll_status ll_attn_sink_window(ll_cache *c, int layer, const void *Q, const void *K_chunk,
                               const void *V_chunk, int n_frames, void *out, void *stream);
+
+/*
+ * ll_attn_sink_window_noalloc -- ll_attn_sink_window for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, computation, results and errors as
+ * ll_attn_sink_window; it allocates nothing and calls no allocating routine.  The
+ * split key walk keeps its partial results and arrival counters in one static device
+ * array per GPU owned by the library (LL_NOALLOC_SCRATCH_BYTES: the partials of
+ * head_dim 128 on a 256-CU device plus 1024 counters, held until the process ends)
+ * instead of the layer's work area.  ll_cache_create sets the array up on its device
+ * (address looked up, counters zeroed before create returns); each merge leaves its
+ * counter at zero again.  All calls of this function on one GPU share the
+ * array, whatever cache or stream they use: calls that overlap in time on one GPU race
+ * (wrong outputs), so issue them in one stream order.  A call whose split walk would
+ * need more than the array holds (a device with more than 256 compute units) returns
+ * LL_ERR_INVALID and launches nothing.
+ * Errors: LL_ERR_INVALID, LL_ERR_HIP.
+ */
+#define LL_NOALLOC_SCRATCH_BYTES (2 * 256 * 256 * 130 * 4 + 1024 * 4)
+ll_status ll_attn_sink_window_noalloc(ll_cache *c, int layer, const void *Q, const void *K_chunk,
+                                      const void *V_chunk, int n_frames, void *out, void *stream);
 
 /*
  * ll_cache_recache -- rewrite the retained cache at a prompt switch.

@@ -7,6 +7,7 @@ provides device memory and streams.  The functions mirror the C ABI declared in
     Cache(layers, heads, head_dim, tokens_per_frame, sink, window, kv_dtype)
     Cache.append(layer, K, V)                      -> ll_cache_append
     Cache.attn(layer, Q, K_chunk, V_chunk, out)    -> ll_attn_sink_window
+    Cache.attn_noalloc(layer, Q, K_chunk, V_chunk, out) -> ll_attn_sink_window_noalloc
     Cache.recache(layer, K_all, V_all)             -> ll_cache_recache
     Cache.recache_window(layer, K_win, V_win)      -> ll_cache_recache_window
     kv_project(h, W_K, W_V, K_all, V_all)          -> ll_kv_project
@@ -26,7 +27,7 @@ _KV_NAMES = {"bf16": LL_KV_BF16, "int8": LL_KV_INT8, "fp8": LL_KV_FP8}
 MAX_SLOTS = 128
 
 EXPORTS = [
-    "ll_cache_create", "ll_cache_destroy", "ll_cache_append", "ll_attn_sink_window",
+    "ll_cache_create", "ll_cache_destroy", "ll_cache_append", "ll_attn_sink_window", "ll_attn_sink_window_noalloc",
     "ll_cache_recache", "ll_cache_recache_window", "ll_kv_project", "ll_cache_recache_from_hidden",
     "ll_cache_create_shots", "ll_cache_begin_shot", "ll_cache_shot_start", "ll_cache_frames_seen",
     "ll_cache_slot_frames", "ll_cache_slot_view", "ll_last_error",
@@ -60,6 +61,7 @@ def lib():
         "ll_cache_destroy": [vp],
         "ll_cache_append": [vp, i32, vp, vp, i32, vp],
         "ll_attn_sink_window": [vp, i32, vp, vp, vp, i32, vp, vp],
+        "ll_attn_sink_window_noalloc": [vp, i32, vp, vp, vp, i32, vp, vp],
         "ll_cache_recache": [vp, i32, vp, vp, i32, vp],
         "ll_cache_recache_window": [vp, i32, vp, vp, i32, vp],
         "ll_kv_project": [vp, vp, vp, i32, i32, i32, vp, vp, vp],
@@ -167,6 +169,15 @@ class Cache:
         n = self._tokens(self._frames(Q, n_frames), Q=Q, K_chunk=K_chunk, V_chunk=V_chunk, out=out)
         _check(lib().ll_attn_sink_window(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n, _ptr(out),
                                          _stream(stream)))
+        return out
+
+    def attn_noalloc(self, layer, Q, K_chunk, V_chunk, out, n_frames=None, stream=None):
+        """ll_attn_sink_window_noalloc: the same attention with the library's static
+        scratch instead of the layer's work area (out must be given: nothing is
+        allocated)."""
+        n = self._tokens(self._frames(Q, n_frames), Q=Q, K_chunk=K_chunk, V_chunk=V_chunk, out=out)
+        _check(lib().ll_attn_sink_window_noalloc(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n,
+                                                 _ptr(out), _stream(stream)))
         return out
 
     def recache(self, layer, K_all, V_all, n_frames=None, stream=None):

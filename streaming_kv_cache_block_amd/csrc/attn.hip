@@ -895,6 +895,23 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
+bool attention_would_split(const AttnParams& p, int D) {
+  // the kernel instance launch_attention picks: 256 query rows per block, or 128 for
+  // chunks of at most 128 rows
+  const int rows = p.nq > 4 * 32 ? kAttnRows : 128;
+  (void)D;
+  Split sp{};
+  sp.n_qtiles = (p.nq + rows - 1) / rows;
+  sp.B = sp.n_qtiles * p.H;
+  sp.J = (p.nq + BN - 1) / BN;
+  for (int k = 0; k < p.nrun; ++k) sp.J += (p.run_rows[k] + BN - 1) / BN;
+  float f = 0.0f;
+  int c = 0;
+  sp.ws = &f;
+  sp.cnt = &c;
+  return plan_split(sp, p.n_cu, split_slots(p.n_cu));
+}
+
 hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t s) {
 // 8 waves of 32 query rows: two waves per SIMD, so one wave's softmax overlaps the
 // other's MFMAs and every accumulator fits the 256 architected VGPRs.

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -144,6 +145,97 @@ ll_status write_frames(ll_cache* c, int layer, const void* K, const void* V, con
   return LL_OK;
 }
 
+// Arguments and parameters of one attention call (shared by the two attention entry
+// points; the work area is filled in by the caller).
+ll_status attn_params(ll_cache* c, int layer, const void* Q, const void* K_chunk, const void* V_chunk, int n_frames,
+                      void* out, ll::AttnParams* pp) {
+  LL_TRY(check_layer(c, layer));
+  LL_TRY(check_tensor(Q, "Q"));
+  LL_TRY(check_tensor(K_chunk, "K_chunk"));
+  LL_TRY(check_tensor(V_chunk, "V_chunk"));
+  LL_TRY(check_tensor(out, "out"));
+  LL_TRY(check_frames(c, n_frames));
+  LL_TRY(check_device(c));
+  const int64_t f0 = c->f0[size_t(layer)];
+  const std::vector<ll::SlotRun> runs = ll::cache_runs(f0, c->layout(), c->fs[size_t(layer)]);
+  ll::AttnParams& p = *pp;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.Kc = static_cast<const uint16_t*>(K_chunk);
+  p.Vc = static_cast<const uint16_t*>(V_chunk);
+  p.out = static_cast<uint16_t*>(out);
+  p.cK = c->k(layer);
+  p.cV = c->v(layer);
+  p.cKs = c->ks(layer);
+  p.cVs = c->vs(layer);
+  p.nq = int(int64_t(n_frames) * c->T);
+  p.ncache = 0;
+  p.nrun = int(runs.size());
+  for (size_t k = 0; k < runs.size(); ++k) {
+    p.run_row0[k] = int(int64_t(runs[k].first) * c->T);
+    p.run_rows[k] = int(int64_t(runs[k].count) * c->T);
+    p.ncache += p.run_rows[k];
+  }
+  p.H = c->heads;
+  p.c = float(1.4426950408889634 / std::sqrt(double(c->head_dim)));
+  p.n_cu = c->n_cu;
+  return LL_OK;
+}
+
+// ---- the allocation-free attention entry point's scratch ------------------------
+// Partial results and arrival counters of the split key walk, for callers that cannot
+// allocate: 2 x 256 partial slots of 256 rows x (128 + 2) floats (head_dim 128 on a
+// 256-CU device; head_dim 64 needs half) and 1024 counters.  One copy per GPU, held
+// until the process ends.  Host code never names the array itself in a launch or copy:
+// it uses the per-device address from hipGetSymbolAddress.
+constexpr int64_t kScratchPartialFloats = int64_t(2) * 256 * (256 * (128 + 2));
+constexpr int kScratchCounters = 1024;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchPartialFloats + kScratchCounters];
+
+namespace {
+
+struct ScratchDevice {
+  float* ptr = nullptr;   // device address of `scratch` on this GPU
+  bool cleared = false;   // counters zeroed (enqueued)
+};
+ScratchDevice g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = int(blockIdx.x) * int(blockDim.x) + int(threadIdx.x);
+  if (i < n) p[i] = 0;
+}
+
+// Set-up of the scratch on `dev` (the current device), once per device: look up the
+// array's address on this GPU (which also makes the runtime load the code object that
+// holds it) and enqueue the zeroing of its counters on stream s (a fill kernel, so that
+// a later call may be captured into a graph).  Done by ll_cache_create, which waits for
+// its stream; the entry point repeats it only for a device no cache was created on.
+ll_status scratch_on_device(int dev, hipStream_t s, float** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(LL_ERR_INVALID, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDevice& d = g_scratch[dev];
+  if (!d.ptr) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    d.ptr = static_cast<float*>(ptr);
+  }
+  if (!d.cleared) {
+    int* cnt = reinterpret_cast<int*>(d.ptr + kScratchPartialFloats);
+    hipLaunchKernelGGL(zero_ints_kernel, dim3((kScratchCounters + 255) / 256), dim3(256), 0, s, cnt,
+                       kScratchCounters);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "clearing the scratch counters");
+    d.cleared = true;
+  }
+  if (out) *out = d.ptr;
+  return LL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,10 +295,20 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
     return fail(LL_ERR_OOM, "hipMalloc of %.3g bytes failed: %s", total, hipGetErrorString(e));
   }
   // Zero the counters on a private stream and wait for that stream only.
+  // The same stream sets up the allocation-free attention's scratch on this device.
   hipStream_t zs = nullptr;
   e = hipStreamCreateWithFlags(&zs, hipStreamNonBlocking);
   if (e == hipSuccess) {
     e = hipMemsetAsync(static_cast<char*>(mem) + cnt_offset, 0, size_t(layers) * size_t(cnt_layer_bytes), zs);
+    if (e == hipSuccess) {
+      const ll_status st = scratch_on_device(dev, zs, nullptr);
+      if (st != LL_OK) {
+        (void)hipStreamSynchronize(zs);
+        (void)hipStreamDestroy(zs);
+        (void)hipFree(mem);
+        return st;
+      }
+    }
     const hipError_t e2 = hipStreamSynchronize(zs);
     if (e == hipSuccess) e = e2;
     const hipError_t e3 = hipStreamDestroy(zs);
@@ -265,40 +367,41 @@ ll_status ll_cache_append(ll_cache* c, int layer, const void* K, const void* V, 
 
 ll_status ll_attn_sink_window(ll_cache* c, int layer, const void* Q, const void* K_chunk, const void* V_chunk,
                               int n_frames, void* out, void* stream) {
-  LL_TRY(check_layer(c, layer));
-  LL_TRY(check_tensor(Q, "Q"));
-  LL_TRY(check_tensor(K_chunk, "K_chunk"));
-  LL_TRY(check_tensor(V_chunk, "V_chunk"));
-  LL_TRY(check_tensor(out, "out"));
-  LL_TRY(check_frames(c, n_frames));
-  LL_TRY(check_device(c));
-  const int64_t f0 = c->f0[size_t(layer)];
-  const std::vector<ll::SlotRun> runs = ll::cache_runs(f0, c->layout(), c->fs[size_t(layer)]);
   ll::AttnParams p{};
-  p.Q = static_cast<const uint16_t*>(Q);
-  p.Kc = static_cast<const uint16_t*>(K_chunk);
-  p.Vc = static_cast<const uint16_t*>(V_chunk);
-  p.out = static_cast<uint16_t*>(out);
-  p.cK = c->k(layer);
-  p.cV = c->v(layer);
-  p.cKs = c->ks(layer);
-  p.cVs = c->vs(layer);
-  p.nq = int(int64_t(n_frames) * c->T);
-  p.ncache = 0;
-  p.nrun = int(runs.size());
-  for (size_t k = 0; k < runs.size(); ++k) {
-    p.run_row0[k] = int(int64_t(runs[k].first) * c->T);
-    p.run_rows[k] = int(int64_t(runs[k].count) * c->T);
-    p.ncache += p.run_rows[k];
-  }
-  p.H = c->heads;
-  p.c = float(1.4426950408889634 / std::sqrt(double(c->head_dim)));
+  LL_TRY(attn_params(c, layer, Q, K_chunk, V_chunk, n_frames, out, &p));
   p.ws = c->ws(layer);
   p.ws_slots = c->ws_slots;
   p.cnt = c->cnt(layer);
-  p.n_cu = c->n_cu;
   hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+ll_status ll_attn_sink_window_noalloc(ll_cache* c, int layer, const void* Q, const void* K_chunk,
+                                      const void* V_chunk, int n_frames, void* out, void* stream) {
+  ll::AttnParams p{};
+  LL_TRY(attn_params(c, layer, Q, K_chunk, V_chunk, n_frames, out, &p));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ll::attention_would_split(p, c->head_dim)) {
+    const int64_t slot_floats = ll::split_slot_floats(c->head_dim, ll::kAttnRows);
+    const int64_t need_floats = ll::split_slots(c->n_cu) * slot_floats;
+    if (need_floats > kScratchPartialFloats || c->n_cu > kScratchCounters)
+      return fail(LL_ERR_INVALID,
+                  "attention without allocation: the split key walk needs %lld bytes of partials and %d "
+                  "counters, the library's static scratch holds %lld bytes and %d",
+                  (long long)(need_floats * 4), c->n_cu, (long long)(kScratchPartialFloats * 4), kScratchCounters);
+    float* base = nullptr;
+    LL_TRY(scratch_on_device(c->device, s, &base));
+    p.ws = base;
+    p.ws_slots = kScratchPartialFloats / slot_floats;
+    p.cnt = reinterpret_cast<int*>(base + kScratchPartialFloats);
+  } else {
+    p.ws = nullptr;   // no split: the launch needs no scratch
+    p.ws_slots = 0;
+    p.cnt = nullptr;
+  }
+  hipError_t e = ll::launch_attention(p, c->head_dim, c->kv_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch (no allocation)");
   return ok();
 }
 

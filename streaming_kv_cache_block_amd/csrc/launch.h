@@ -49,6 +49,10 @@ constexpr int kAttnRows = 256;
 // kv_fmt: 0 bf16 cache, 1 int8 codes, 2 fp8 (E4M3) codes (+ fp32 scales).
 hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t s);
 
+// Whether launch_attention would split the key walk of p (given a large enough work
+// area): the blocks leave CUs idle and the walk is long enough.
+bool attention_would_split(const AttnParams& p, int D);
+
 // Copy (bf16) or quantise (int8 / fp8) whole frames of a [frames*T][H][D] bf16 tensor into
 // cache slots.  plan_src[i] is the frame index in the source tensor, plan_slot[i] the
 // destination slot, for i < n.

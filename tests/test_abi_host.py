@@ -70,6 +70,7 @@ def test_calls_on_null_handle_are_invalid(L):
     p16 = (p + 15) // 16 * 16
     assert L.ll_cache_append(None, 0, p16, p16, 1, None) == ll.LL_ERR_INVALID
     assert L.ll_attn_sink_window(None, 0, p16, p16, p16, 1, p16, None) == ll.LL_ERR_INVALID
+    assert L.ll_attn_sink_window_noalloc(None, 0, p16, p16, p16, 1, p16, None) == ll.LL_ERR_INVALID
     assert L.ll_cache_recache(None, 0, p16, p16, 1, None) == ll.LL_ERR_INVALID
     assert L.ll_cache_recache_window(None, 0, p16, p16, 1, None) == ll.LL_ERR_INVALID
     assert L.ll_cache_recache_from_hidden(None, 0, p16, p16, p16, 1, 128, None) == ll.LL_ERR_INVALID
