@@ -9,11 +9,15 @@ tensors generated on the device before the timed region (a pool of fresh Q/K/V
 sets, one per pass, reused cyclically across steps).
 
 Prints ONE JSON line with the whole-step throughput in latent frames/s per layer,
-the attention kernel's roofline position, component timings (int8 and fp8 caches,
-recache projection, rewrite and the fused projection-into-slots) and the CPU oracle
-timed on this host as a baseline.
+the attention kernel's roofline position, component timings (per-kernel median /
+p10 / p90; int8 and fp8 caches; warm and cold appends; the 30-layer rollout, the
+30-layer recache at a prompt switch and the 400-chunk int8 rollout with recache;
+the shader clock read during the timed work) and the CPU oracle timed on this host
+as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--no-components] [--no-rollouts]
+                    [--workload steady|rollout|long_int8|recache|sweep|append]
 """
 
 import argparse
@@ -21,6 +25,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +43,7 @@ def _events(torch, n):
 
 def _kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("attn.hip", "device_common.h", "launch.h"):
+    for f in ("attn.hip", "device_common.h", "launch.h", "split_plan.h"):
         with open(os.path.join(ROOT, "streaming_kv_cache_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -62,11 +67,89 @@ def _attn_flops(H, D, nq, nk):
     return 4.0 * H * D * nq * nk
 
 
-def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
+def _append_bytes(rows, D, kv):
+    """Algorithmic bytes of writing `rows` (token, head) rows of K and V into slots: the
+    bf16 inputs read, the slot codes written and, for int8 / fp8, one fp32 scale per row."""
+    elt = 1 if kv != "bf16" else 2
+    return 2 * rows * D * 2 + 2 * rows * D * elt + (2 * rows * 4 if kv != "bf16" else 0)
+
+
+def _stats(xs):
+    """mean / median / p10 / p90 / min of a list of durations (same unit)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "min": float(a.min()), "n": int(a.size)}
+
+
+class ClockSampler:
+    """Reads the GPU's shader clock with amdsmi on a background thread while timed work
+    runs (context manager): the mean over the 8 XCDs of the metrics table's current GFX
+    clocks, kept only while the GFX activity reads >= 90% (the table lags the load by
+    tens of ms).  summary() gives median / min / max in MHz, or why it could not be read."""
+
+    def __init__(self, period_s=0.01):
+        self.period = period_s
+        self.samples = []
+        self.seen = 0
+        self.err = None
+        self._stop = threading.Event()
+        self._th = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self._smi, self._h = amdsmi, handles[0]
+            self._read()
+        except Exception as e:   # the clock is context; its absence is reported, not fatal
+            self.err = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [float(c) for c in m.get("current_gfxclks", []) if isinstance(c, (int, float))]
+        act = m.get("average_gfx_activity")
+        return (sum(clks) / len(clks) if clks else None), act
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                clk, act = self._read()
+                self.seen += 1
+                if clk is not None and isinstance(act, (int, float)) and act >= 90:
+                    self.samples.append(clk)
+            except Exception as e:
+                self.err = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.err is None:
+            self._th = threading.Thread(target=self._loop, daemon=True)
+            self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._th is not None:
+            self._th.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"error": self.err or f"no sample at >= 90% GFX activity ({self.seen} read)"}
+        import numpy as np
+        a = np.asarray(self.samples)
+        return {"median_mhz": float(np.median(a)), "min_mhz": float(a.min()), "max_mhz": float(a.max()),
+                "samples": int(a.size), "source": "amdsmi gpu metrics: mean of the 8 XCDs' current GFX clocks, "
+                                                  "samples at >= 90% GFX activity"}
+
+
+def run_steady(torch, ll, synth, cfg, steps, warmup, kv="bf16"):
     """The timed step loop (nothing but the steps between the two synchronisations),
     then as many steps again with HIP events around each launch for the per-kernel
     times; returns a dict of measurements."""
-    kv = kv or ("int8" if kv_int8 else "bf16")
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     shape = (cfg.nq, H, D)
     cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
@@ -111,21 +194,40 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv_int8=False, kv=None):
         step(i, True)
     torch.cuda.synchronize()
     attn_ms = [a0[j].elapsed_time(a1[j]) for j in range(steps * P)]
+    # the shader clock under this attention pass: about one second more of the same
+    # launches (not part of any figure above) while the clock is sampled
+    with ClockSampler() as clk:
+        for i in range(max(1, int(1000.0 / max(sum(attn_ms) / len(attn_ms), 0.01)))):
+            cache.attn(0, *pool[i % POOL], out)
+        torch.cuda.synchronize()
     app_ms = [b0[i].elapsed_time(b1[i]) for i in range(steps)]
-    elt = 1 if kv != "bf16" else 2
-    rows = C * T * H
-    app_bytes = 2 * rows * D * 2 + 2 * rows * D * elt + (2 * rows * 4 if kv != "bf16" else 0)
+    app_bytes = _append_bytes(C * T * H, D, kv)
     attn_avg = sum(attn_ms) / len(attn_ms)
     app_avg = sum(app_ms) / len(app_ms)
     flops = _attn_flops(H, D, cfg.nq, nk)
     cache.close()
     return {
         "wall_s": wall, "keys": nk, "cached_keys": n_vis * T,
-        "attn_ms": attn_avg, "attn_ms_min": min(attn_ms),
+        "attn_ms": attn_avg, "attn_ms_stats": _stats(attn_ms),
         "attn_tflops": flops / attn_avg / 1e9, "attn_flops": flops,
-        "append_us": app_avg * 1e3, "append_bytes": app_bytes,
-        "append_gbs": app_bytes / app_avg / 1e6,
+        "append_us": app_avg * 1e3, "append_us_stats": _stats([x * 1e3 for x in app_ms]), "append_bytes": app_bytes,
+        "append_gbs": app_bytes / app_avg / 1e6, "sclk": clk.summary(),
     }
+
+
+def _attention_component(r):
+    st = r["attn_ms_stats"]
+    return {"ms": r["attn_ms"], "ms_median": st["median"], "ms_p10": st["p10"], "ms_p90": st["p90"],
+            "tflops": r["attn_tflops"], "tflops_at_median": r["attn_flops"] / st["median"] / 1e9,
+            "frac_mfma": r["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r["keys"], "sclk": r["sclk"]}
+
+
+def _append_component(r):
+    st = r["append_us_stats"]
+    return {"us": r["append_us"], "us_median": st["median"], "us_p10": st["p10"], "us_p90": st["p90"],
+            "gbs": r["append_gbs"], "frac_hbm": r["append_gbs"] / PEAK_HBM_GBS, "bytes": r["append_bytes"],
+            "note": "HIP events around each launch inside the step (includes dispatch after the attention kernel); "
+                    "the inputs were just read by the attention passes, so they are warm in the Infinity Cache"}
 
 
 def run_copy_reference(torch, cfg, n=40):
@@ -149,11 +251,8 @@ def run_copy_reference(torch, cfg, n=40):
     return {"us": us, "gbs": byt / us / 1e3, "frac_hbm": byt / us / 1e3 / PEAK_HBM_GBS, "bytes": byt}
 
 
-def run_append_batch(torch, ll, synth, cfg, kv="bf16", window=None, n=40):
-    """n appends of one chunk issued back to back between one pair of events: the
-    kernel's own throughput, without the event bracketing of a single launch."""
+def _append_cache(torch, ll, synth, cfg, kv, W):
     C, T, H, D, S = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink
-    W = cfg.window if window is None else window
     shape = (cfg.nq, H, D)
     cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
     pool = [tuple(synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, t, 2000 + i) for t in range(2))
@@ -161,6 +260,15 @@ def run_append_batch(torch, ll, synth, cfg, kv="bf16", window=None, n=40):
     for i in range((S + W + C - 1) // C + 1):
         cache.append(0, *pool[i % POOL])
     torch.cuda.synchronize()
+    return cache, pool
+
+
+def run_append_batch(torch, ll, synth, cfg, kv="bf16", window=None, n=40):
+    """n appends of one chunk issued back to back between one pair of events: the
+    kernel's own throughput, without the event bracketing of a single launch (the pool
+    of 8 input chunks, 230 MB, stays partly in the Infinity Cache)."""
+    W = cfg.window if window is None else window
+    cache, pool = _append_cache(torch, ll, synth, cfg, kv, W)
     e0, e1 = _events(torch, 1)[0], _events(torch, 1)[0]
     e0.record()
     for i in range(n):
@@ -168,17 +276,40 @@ def run_append_batch(torch, ll, synth, cfg, kv="bf16", window=None, n=40):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / n * 1e3
-    rows = C * T * H
-    elt = 1 if kv != "bf16" else 2
-    byt = 2 * rows * D * 2 + 2 * rows * D * elt + (2 * rows * 4 if kv != "bf16" else 0)
+    byt = _append_bytes(cfg.chunk_frames * cfg.tokens_per_frame * cfg.heads, cfg.head_dim, kv)
     cache.close()
     return {"us": us, "gbs": byt / us / 1e3, "frac_hbm": byt / us / 1e3 / PEAK_HBM_GBS, "bytes": byt}
 
 
+def run_append_cold(torch, ll, synth, cfg, kv="bf16", window=None, n=20):
+    """Appends with the caches flushed first: before each one a 1 GiB buffer is read
+    (four times the 256 MB Infinity Cache, and every L2; read, so that no dirty lines
+    are left to write back during the append), outside the events; each append is
+    timed alone with events around its launch."""
+    W = cfg.window if window is None else window
+    cache, pool = _append_cache(torch, ll, synth, cfg, kv, W)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    e0, e1 = _events(torch, n), _events(torch, n)
+    for i in range(n):
+        flush.sum()
+        e0[i].record()
+        cache.append(0, *pool[i % POOL])
+        e1[i].record()
+    torch.cuda.synchronize()
+    us = [e0[i].elapsed_time(e1[i]) * 1e3 for i in range(n)]
+    st = _stats(us)
+    byt = _append_bytes(cfg.chunk_frames * cfg.tokens_per_frame * cfg.heads, cfg.head_dim, kv)
+    cache.close()
+    del flush
+    return {"us_median": st["median"], "us_p10": st["p10"], "us_p90": st["p90"], "bytes": byt,
+            "gbs_at_median": byt / st["median"] / 1e3, "frac_hbm_at_median": byt / st["median"] / 1e3 / PEAK_HBM_GBS,
+            "note": "Infinity Cache and L2 flushed (1 GiB read) before each append; events around the single launch"}
+
+
 def run_recache_layer(torch, ll, synth, cfg, reps=10):
-    """Recache of one layer at the recache workload's size, bf16 and int8 caches:
+    """Recache of one layer at the recache workload's size, bf16, int8 and fp8 caches:
     projection GEMM then rewrite (two launches, K/V round trip through HBM), and the
-    fused projection whose epilogue writes the slots."""
+    fused projection whose epilogue writes the slots; per-launch medians / p10 / p90."""
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     hid = cfg.hidden
     shape = (cfg.nq, H, D)
@@ -208,26 +339,73 @@ def run_recache_layer(torch, ll, synth, cfg, reps=10):
             cache.recache_from_hidden(0, h, wk, wv)
             f1[i].record()
         torch.cuda.synchronize()
-        gms = sum(g0[i].elapsed_time(g1[i]) for i in range(reps)) / reps
-        rms = sum(r0[i].elapsed_time(r1[i]) for i in range(reps)) / reps
-        fms = sum(f0[i].elapsed_time(f1[i]) for i in range(reps)) / reps
+        gst = _stats([g0[i].elapsed_time(g1[i]) for i in range(reps)])
+        rst = _stats([r0[i].elapsed_time(r1[i]) * 1e3 for i in range(reps)])
+        fst = _stats([f0[i].elapsed_time(f1[i]) for i in range(reps)])
         flops = 2.0 * 2 * n * T * hid * hid
-        elt = 2 if kv == "bf16" else 1
-        # rewrite: read bf16 K/V, write slots (+ int8 scales)
-        wbytes = 2 * n * T * H * D * elt + (2 * n * T * H * 4 if kv == "int8" else 0)
-        rbytes = 2 * n * T * H * D * 2 + wbytes
+        rbytes = _append_bytes(n * T * H, D, kv)
         cache.close()
         if kv == "bf16":
-            res.update({"proj_ms": gms, "proj_tflops": flops / gms / 1e9,
-                        "proj_frac": flops / gms / 1e9 / PEAK_BF16_TFLOPS,
-                        "rewrite_us": rms * 1e3, "rewrite_bytes": rbytes, "rewrite_gbs": rbytes / rms / 1e6,
-                        "rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
-        else:
-            res.update({f"{kv}_rewrite_us": rms * 1e3, f"{kv}_rewrite_gbs": rbytes / rms / 1e6,
-                        f"{kv}_rewrite_frac": rbytes / rms / 1e6 / PEAK_HBM_GBS})
-        res[f"{kv}_unfused_ms"] = gms + rms
-        res[f"{kv}_fused_ms"] = fms
-        res[f"{kv}_fused_tflops"] = flops / fms / 1e9
+            res["projection"] = {"ms": gst["mean"], "ms_median": gst["median"], "ms_p10": gst["p10"],
+                                 "ms_p90": gst["p90"], "tflops": flops / gst["mean"] / 1e9,
+                                 "frac_mfma": flops / gst["mean"] / 1e9 / PEAK_BF16_TFLOPS, "flop": flops}
+        res[f"rewrite_{kv}"] = {"us": rst["mean"], "us_median": rst["median"], "us_p10": rst["p10"],
+                                "us_p90": rst["p90"], "bytes": rbytes, "gbs": rbytes / rst["mean"] / 1e3,
+                                "frac_hbm": rbytes / rst["mean"] / 1e3 / PEAK_HBM_GBS}
+        res[f"fused_{kv}"] = {"ms": fst["mean"], "ms_median": fst["median"], "unfused_ms": gst["mean"] + rst["mean"] / 1e3,
+                              "tflops": flops / fst["mean"] / 1e9}
+    return res
+
+
+def run_recache_stack(torch, ll, synth, cfg):
+    """The prompt switch of the recache workload on all of its layers: a 30-layer cache
+    with 6 seeded chunks appended (ring wrapped), then every layer recomputes its K/V
+    from its own hidden states and weights and rewrites its 15 slots -- projection then
+    rewrite, or the fused projection into the slots -- then the next chunk's attention
+    on every layer.  bf16, int8 and fp8 caches; each stack timed between one pair of
+    events."""
+    C, T, H, D, S, W, L = (cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window,
+                           cfg.layers)
+    hid = cfg.hidden
+    shape = (cfg.nq, H, D)
+    n = min(cfg.prefill_chunks * C, S + W)
+    hs = [synth.normal_bf16_device((n * T, hid), 1.0, cfg.seed, 10, l) for l in range(L)]
+    ws = [(synth.normal_bf16_device((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 11, l),
+           synth.normal_bf16_device((hid, hid), (1.0 / hid) ** 0.5, cfg.seed, 12, l)) for l in range(L)]
+    pool = [tuple(synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, t, 3000 + i) for t in range(3))
+            for i in range(4)]
+    K = torch.empty((n * T, H * D), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(K)
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    res = {"workload": cfg.name, "layers": L, "retained_frames": n}
+    flops = 2.0 * 2 * n * T * hid * hid * L
+    for kv in ("bf16", "int8", "fp8"):
+        cache = ll.Cache(L, H, D, T, S, W, kv_dtype=kv)
+        for l in range(L):
+            for k in range(cfg.prefill_chunks):
+                cache.append(l, pool[k % 4][1], pool[k % 4][2])
+        torch.cuda.synchronize()
+        e = _events(torch, 6)
+        with ClockSampler() as clk:
+            e[0].record()
+            for l in range(L):
+                ll.kv_project(hs[l], *ws[l], K, V)
+                cache.recache(l, K, V)
+            e[1].record()
+            e[2].record()
+            for l in range(L):
+                cache.recache_from_hidden(l, hs[l], *ws[l])
+            e[3].record()
+            e[4].record()
+            for l in range(L):
+                cache.attn(l, *pool[l % 4], out)
+            e[5].record()
+            torch.cuda.synchronize()
+        unf, fus, att = (e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(3))
+        res[kv] = {"stack_ms_unfused": unf, "stack_ms_fused": fus, "next_chunk_attention_ms": att,
+                   "fused_tflops": flops / fus / 1e9, "rewrite_bytes": L * _append_bytes(n * T * H, D, kv),
+                   "sclk": clk.summary()}
+        cache.close()
     return res
 
 
@@ -237,7 +415,8 @@ def run_rollout(torch, ll, synth, cfg):
     Inputs come from a pool of seeded device tensors made before timing."""
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     shape = (cfg.nq, H, D)
-    cache = ll.Cache(cfg.layers, H, D, T, S, W, kv_dtype="int8" if cfg.kv_int8 else "bf16")
+    kv = "int8" if cfg.kv_int8 else "bf16"
+    cache = ll.Cache(cfg.layers, H, D, T, S, W, kv_dtype=kv)
     pool = [tuple(synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, t, 2000 + i) for t in range(3))
             for i in range(POOL)]
     n_re = S + W
@@ -249,33 +428,38 @@ def run_rollout(torch, ll, synth, cfg):
     torch.cuda.synchronize()
     e0, e1 = _events(torch, 2)
     flops = 0.0
-    t0 = time.perf_counter()
-    e0.record()
+    app_bytes = 0
     i = 0
-    for k in range(cfg.chunks):
-        if rec is not None and k > 0 and k % cfg.recache_every == 0:
+    with ClockSampler(period_s=0.05) as clk:
+        t0 = time.perf_counter()
+        e0.record()
+        for k in range(cfg.chunks):
+            if rec is not None and k > 0 and k % cfg.recache_every == 0:
+                for l in range(cfg.layers):
+                    cache.recache(l, *rec)
+            n_vis = min(cache.frames_seen(0), S + W)
+            for p in range(cfg.passes):
+                for l in range(cfg.layers):
+                    q, kk, vv = pool[i % POOL]
+                    i += 1
+                    cache.attn(l, q, kk, vv, out)
+            flops += cfg.passes * cfg.layers * _attn_flops(H, D, cfg.nq, (n_vis + C) * T)
             for l in range(cfg.layers):
-                cache.recache(l, *rec)
-        n_vis = min(cache.frames_seen(0), S + W)
-        for p in range(cfg.passes):
-            for l in range(cfg.layers):
-                q, kk, vv = pool[i % POOL]
-                i += 1
-                cache.attn(l, q, kk, vv, out)
-        flops += cfg.passes * cfg.layers * _attn_flops(H, D, cfg.nq, (n_vis + C) * T)
-        for l in range(cfg.layers):
-            cache.append(l, kk, vv)
-        if k % 20 == 19:
-            print(f"# {cfg.name}: chunk {k + 1}/{cfg.chunks}", file=sys.stderr, flush=True)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+                cache.append(l, kk, vv)
+            app_bytes += cfg.layers * _append_bytes(C * T * H, D, kv)
+            if k % 20 == 19:
+                print(f"# {cfg.name}: chunk {k + 1}/{cfg.chunks}", file=sys.stderr, flush=True)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     gpu_s = e0.elapsed_time(e1) / 1e3
     frames = cfg.chunks * C
     cache.close()
-    return {"workload": cfg.name, "layers": cfg.layers, "latent_frames": frames, "seconds": gpu_s, "wall_s": wall,
-            "latent_frames_per_s_stack": frames / gpu_s, "latent_frames_per_s_per_layer": frames * cfg.layers / gpu_s,
-            "attention_flop": flops, "avg_tflops_incl_append": flops / gpu_s / 1e12}
+    return {"workload": cfg.name, "layers": cfg.layers, "kv": kv, "latent_frames": frames, "seconds": gpu_s,
+            "wall_s": wall, "latent_frames_per_s_stack": frames / gpu_s,
+            "latent_frames_per_s_per_layer": frames * cfg.layers / gpu_s, "attention_flop": flops,
+            "append_bytes": app_bytes, "avg_tflops_incl_append": flops / gpu_s / 1e12,
+            "recaches": (cfg.chunks - 1) // cfg.recache_every if cfg.recache_every else 0, "sclk": clk.summary()}
 
 
 def run_window_sweep(torch, ll, synth, base, steps=10):
@@ -297,14 +481,14 @@ def run_window_sweep(torch, ll, synth, base, steps=10):
     return res
 
 
-def run_recache_stack(torch, ll, synth, cfg, reps=3):
-    """Recache of every layer at a prompt switch: per layer either projection then
-    rewrite, or the fused projection-into-slots (bf16 and int8 caches)."""
-    r = run_recache_layer(torch, ll, synth, cfg, reps=reps)
-    out = {"workload": cfg.name, "layers": cfg.layers, "per_layer": r}
-    for kv in ("bf16", "int8", "fp8"):
-        out[f"stack_ms_{kv}_unfused"] = cfg.layers * r[f"{kv}_unfused_ms"]
-        out[f"stack_ms_{kv}_fused"] = cfg.layers * r[f"{kv}_fused_ms"]
+def run_appends(torch, ll, synth, cfg, n=40):
+    """Appends only (for a kernel trace of the cache writes): per format, n warm appends
+    back to back, then cold appends with the caches flushed in between."""
+    i8w = configs_mod().LONG_INT8.window
+    out = {}
+    for kv, W in (("bf16", cfg.window), ("int8", i8w), ("fp8", i8w)):
+        out[f"{kv}_w{W}_back_to_back"] = run_append_batch(torch, ll, synth, cfg, kv, W, n)
+        out[f"{kv}_w{W}_cold"] = run_append_cold(torch, ll, synth, cfg, kv, W)
     return out
 
 
@@ -313,28 +497,47 @@ def configs_mod():
     return configs
 
 
-def cpu_baseline(cfg):
-    """The CPU oracle as it stands, on one full steady-state step (4 passes over all
-    4680 query rows x 12 heads, then the append bookkeeping), on this host."""
-    import numpy as np  # noqa: F401
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, full=True):
+    """The CPU oracle as it stands, timed on this host.  The value: one full steady-state
+    step (all passes over all 4680 query rows x 12 heads, then the append bookkeeping).
+    With full=True also, each labelled: the toy workload end to end; one layer of the
+    recache workload (projection and the slot-model rewrite); and the per-row cost of the
+    sampled-row checks of the 30-layer rollouts, extrapolated to the whole rollouts."""
+    import numpy as np
     import synth
-    from oracle import attention, ring
+    from oracle import attention, gemm, ring
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
+    configs = configs_mod()
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     shape = (cfg.nq, H, D)
-    model = ring.RingModel(S, W)
-    frames = {}
-    prefill = (S + W + C - 1) // C + 1
-    for k in range(prefill):
-        kb = synth.normal_bf16(shape, cfg.sigma, cfg.seed, 901, k)
-        vb = synth.normal_bf16(shape, cfg.sigma, cfg.seed, 902, k)
-        for i in range(C):
-            frames[model.f0 + i] = (kb[i * T:(i + 1) * T], vb[i * T:(i + 1) * T])
-        model.append(C)
+
+    def steady_history(S, W, n_chunks, seed):
+        model = ring.RingModel(S, W)
+        frames = {}
+        for k in range(n_chunks):
+            kb = synth.normal_bf16(shape, cfg.sigma, seed, 901, k)
+            vb = synth.normal_bf16(shape, cfg.sigma, seed, 902, k)
+            for i in range(C):
+                frames[model.f0 + i] = (kb[i * T:(i + 1) * T], vb[i * T:(i + 1) * T])
+            model.append(C)
+        return model, frames
+
+    model, frames = steady_history(S, W, (S + W + C - 1) // C + 1, cfg.seed)
     inputs = [tuple(synth.normal_bf16(shape, cfg.sigma, cfg.seed, 903, t, p) for t in range(3))
               for p in range(cfg.passes)]
     t0 = time.perf_counter()
@@ -342,10 +545,73 @@ def cpu_baseline(cfg):
         attention.chunk_attention(q, k, v, frames.__getitem__, model.f0, S, W, T)
     model.append(C)
     dt = time.perf_counter() - t0
-    return {"value": C / dt, "unit": "latent frames/s per layer", "cores": threads, "kind": "oracle",
-            "sample": f"one full steady-state step: {cfg.passes} passes x {cfg.nq} query rows x {H} heads "
-                      f"over {(min(model.f0 - C, S + W) + C) * T} keys, then the append (fp32 numpy)",
-            "seconds": dt}
+    out = {"value": C / dt, "unit": "latent frames/s per layer", "cores": threads, "kind": "oracle",
+           "sample": f"one full steady-state step: {cfg.passes} passes x {cfg.nq} query rows x {H} heads "
+                     f"over {(min(model.f0 - C, S + W) + C) * T} keys, then the append (fp32 numpy)",
+           "seconds": dt, "extrapolated": False, "cpu_model": _cpu_model()}
+    if not full:
+        return out
+    pieces = {}
+    # toy workload end to end: every pass of every chunk, append bookkeeping
+    toy = configs.TOY
+    tshape = (toy.nq, toy.heads, toy.head_dim)
+    tm = ring.RingModel(toy.sink, toy.window)
+    tframes = {}
+    t0 = time.perf_counter()
+    for k in range(toy.chunks):
+        for p in range(toy.passes):
+            q, kc, vc = (synth.normal_bf16(tshape, toy.sigma, toy.seed, t, 0, k, p) for t in range(3))
+            attention.chunk_attention(q, kc, vc, tframes.__getitem__, tm.f0, toy.sink, toy.window,
+                                      toy.tokens_per_frame)
+        for i in range(toy.chunk_frames):
+            tframes[tm.f0 + i] = (kc[i * toy.tokens_per_frame:(i + 1) * toy.tokens_per_frame],
+                                  vc[i * toy.tokens_per_frame:(i + 1) * toy.tokens_per_frame])
+        tm.append(toy.chunk_frames)
+    pieces["toy_end_to_end"] = {"seconds": time.perf_counter() - t0, "extrapolated": False,
+                                "what": f"{toy.chunks} chunks x {toy.passes} passes + appends"}
+    # one layer of the recache workload: the projection (fp32 numpy) and the slot-model rewrite
+    rc = configs.RECACHE
+    n = min(rc.prefill_chunks * rc.chunk_frames, rc.sink + rc.window)
+    h = synth.normal_bf16((n * rc.tokens_per_frame, rc.hidden), 1.0, rc.seed, 10, 0)
+    wk = synth.normal_bf16((rc.hidden, rc.hidden), (1.0 / rc.hidden) ** 0.5, rc.seed, 11, 0)
+    wv = synth.normal_bf16((rc.hidden, rc.hidden), (1.0 / rc.hidden) ** 0.5, rc.seed, 12, 0)
+    t0 = time.perf_counter()
+    gemm.project_bf16(h, wk)
+    gemm.project_bf16(h, wv)
+    tg = time.perf_counter() - t0
+    rm = ring.RingModel(rc.sink, rc.window)
+    rm.append(rc.prefill_chunks * rc.chunk_frames)
+    t0 = time.perf_counter()
+    rm.recache(n)
+    pieces["recache_one_layer"] = {"seconds": tg + time.perf_counter() - t0, "projection_seconds": tg,
+                                   "extrapolated": False,
+                                   "what": f"K and V projections of {n * rc.tokens_per_frame} x {rc.hidden} hidden "
+                                           f"states, then the rewrite of {n} slots in the slot model"}
+    # rollouts: per-row cost of the sampled-row checks, fitted as a + b rows per
+    # (chunk, pass, layer) call at the steady-state key count, extrapolated
+    for name, wl in (("rollout_30_layers_extrapolated", configs.ROLLOUT),
+                     ("long_int8_rollout_extrapolated", configs.LONG_INT8)):
+        kv = "int8" if wl.kv_int8 else "bf16"
+        m2, fr2 = steady_history(wl.sink, wl.window, (wl.sink + wl.window + C - 1) // C + 1, wl.seed)
+        q, kc, vc = inputs[0]
+        ts = {}
+        for nrows in (16, 64):
+            rows = list(range(0, cfg.nq, cfg.nq // nrows))[:nrows]
+            t0 = time.perf_counter()
+            attention.chunk_attention(q, kc, vc, fr2.__getitem__, m2.f0, wl.sink, wl.window, T, kv=kv, rows=rows)
+            ts[nrows] = time.perf_counter() - t0
+        b = max((ts[64] - ts[16]) / 48, 0.0)
+        a = max(ts[16] - 16 * b, 0.0)
+        per_call = a + b * cfg.nq
+        calls = wl.chunks * wl.passes * wl.layers
+        pieces[name] = {"seconds": per_call * calls, "extrapolated": True,
+                        "per_call_seconds": per_call, "calls": calls,
+                        "what": f"oracle on 16 and 64 sampled query rows at the full key count ({kv} cache), "
+                                f"fitted per call and multiplied by {wl.chunks} chunks x {wl.passes} passes x "
+                                f"{wl.layers} layers (early chunks see fewer keys: an overestimate); appends and "
+                                f"recaches not counted"}
+    out["pieces"] = pieces
+    return out
 
 
 def main():
@@ -355,10 +621,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
-    ap.add_argument("--workload", default="steady", choices=["steady", "rollout", "long_int8", "recache", "sweep"],
+    ap.add_argument("--no-rollouts", action="store_true",
+                    help="leave the 30-layer rollout, the 30-layer recache and the 400-chunk int8 rollout out of "
+                         "the components")
+    ap.add_argument("--workload", default="steady",
+                    choices=["steady", "rollout", "long_int8", "recache", "sweep", "append", "steady_int8",
+                             "steady_fp8"],
                     help="steady (default): the one-chunk step below; the others print their own "
                          "JSON record: 30-layer rollout, 400-chunk int8 rollout with recache, "
-                         "30-layer recache, window/sink sweep")
+                         "30-layer recache, window/sink sweep, appends only (warm and cold), the "
+                         "steady step with an int8 / fp8 cache at window 21 (for counter runs)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -393,6 +665,14 @@ def main():
             rec = run_rollout(torch, ll, synth, configs.LONG_INT8)
         elif args.workload == "recache":
             rec = run_recache_stack(torch, ll, synth, configs.RECACHE)
+        elif args.workload == "append":
+            rec = {"workload": "appends", "rows": run_appends(torch, ll, synth, configs.STEADY)}
+        elif args.workload in ("steady_int8", "steady_fp8"):
+            kv = args.workload.split("_")[1]
+            w = configs.Workload(**{**configs.STEADY.__dict__, "window": configs.LONG_INT8.window,
+                                    "name": f"steady_h12_d128_t1560_s3_w21_{kv}"})
+            r = run_steady(torch, ll, synth, w, args.steps, args.warmup, kv=kv)
+            rec = {"workload": w.name, "attention": _attention_component(r), "append": _append_component(r)}
         else:
             rec = {"workload": "window_sink_sweep", "rows": run_window_sweep(torch, ll, synth, configs.STEADY)}
         print(json.dumps(rec), flush=True)
@@ -407,36 +687,33 @@ def main():
     if not args.no_components:
         i8 = configs.Workload(**{**cfg.__dict__, "window": configs.LONG_INT8.window, "kv_int8": True,
                                  "seed": configs.LONG_INT8.seed})
-        r8 = run_steady(torch, ll, synth, i8, max(5, args.steps // 5), 2, kv="int8")
-        rf8 = run_steady(torch, ll, synth, i8, max(5, args.steps // 5), 2, kv="fp8")
+        ksteps = max(5, args.steps // 5)
+        r8 = run_steady(torch, ll, synth, i8, ksteps, 2, kv="int8")
+        rf8 = run_steady(torch, ll, synth, i8, ksteps, 2, kv="fp8")
         rc = run_recache_layer(torch, ll, synth, configs.RECACHE)
         components = {
-            "attention_bf16": {"ms": r["attn_ms"], "tflops": r["attn_tflops"],
-                               "frac_mfma": r["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r["keys"]},
-            "append_bf16": {"us": r["append_us"], "gbs": r["append_gbs"],
-                            "frac_hbm": r["append_gbs"] / PEAK_HBM_GBS, "bytes": r["append_bytes"]},
+            "attention_bf16": _attention_component(r),
+            "append_bf16": _append_component(r),
             "append_bf16_back_to_back": run_append_batch(torch, ll, synth, cfg),
+            "append_bf16_cold": run_append_cold(torch, ll, synth, cfg),
             "copy_reference_same_bytes": run_copy_reference(torch, cfg),
-            "attention_int8_w21": {"ms": r8["attn_ms"], "tflops": r8["attn_tflops"],
-                                   "frac_mfma": r8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": r8["keys"]},
-            "append_int8_w21": {"us": r8["append_us"], "gbs": r8["append_gbs"],
-                                "frac_hbm": r8["append_gbs"] / PEAK_HBM_GBS, "bytes": r8["append_bytes"]},
+            "attention_int8_w21": _attention_component(r8),
+            "append_int8_w21": _append_component(r8),
             "append_int8_w21_back_to_back": run_append_batch(torch, ll, synth, cfg, "int8", i8.window),
-            "attention_fp8_w21": {"ms": rf8["attn_ms"], "tflops": rf8["attn_tflops"],
-                                  "frac_mfma": rf8["attn_tflops"] / PEAK_BF16_TFLOPS, "keys": rf8["keys"]},
-            "append_fp8_w21": {"us": rf8["append_us"], "gbs": rf8["append_gbs"],
-                               "frac_hbm": rf8["append_gbs"] / PEAK_HBM_GBS, "bytes": rf8["append_bytes"]},
+            "append_int8_w21_cold": run_append_cold(torch, ll, synth, cfg, "int8", i8.window),
+            "attention_fp8_w21": _attention_component(rf8),
+            "append_fp8_w21": _append_component(rf8),
             "append_fp8_w21_back_to_back": run_append_batch(torch, ll, synth, cfg, "fp8", i8.window),
-            "recache_projection": {"ms": rc["proj_ms"], "tflops": rc["proj_tflops"], "frac_mfma": rc["proj_frac"]},
-            "recache_rewrite": {"us": rc["rewrite_us"], "gbs": rc["rewrite_gbs"], "frac_hbm": rc["rewrite_frac"],
-                                "bytes": rc["rewrite_bytes"]},
-            "recache_int8_rewrite": {"us": rc["int8_rewrite_us"], "gbs": rc["int8_rewrite_gbs"],
-                                     "frac_hbm": rc["int8_rewrite_frac"]},
-            "recache_fp8_rewrite": {"us": rc["fp8_rewrite_us"], "gbs": rc["fp8_rewrite_gbs"],
-                                    "frac_hbm": rc["fp8_rewrite_frac"]},
-            "recache_fused": {kv: {"ms": rc[f"{kv}_fused_ms"], "unfused_ms": rc[f"{kv}_unfused_ms"],
-                                   "tflops": rc[f"{kv}_fused_tflops"]} for kv in ("bf16", "int8", "fp8")},
+            "append_fp8_w21_cold": run_append_cold(torch, ll, synth, cfg, "fp8", i8.window),
+            "recache_layer": rc,
         }
+        if not args.no_rollouts:
+            print("# components: 30-layer rollout", file=sys.stderr, flush=True)
+            components["rollout_30_layers_80_chunks"] = run_rollout(torch, ll, synth, configs.ROLLOUT)
+            print("# components: 30-layer recache", file=sys.stderr, flush=True)
+            components["recache_30_layers"] = run_recache_stack(torch, ll, synth, configs.RECACHE)
+            print("# components: 400-chunk int8 rollout", file=sys.stderr, flush=True)
+            components["long_int8_rollout_400_chunks"] = run_rollout(torch, ll, synth, configs.LONG_INT8)
 
     line = {
         "metric": METRIC,
@@ -459,11 +736,13 @@ def main():
                      "unit": "TFLOP/s", "frac": r["attn_tflops"] / PEAK_BF16_TFLOPS,
                      "traffic": _traffic_from_profiles(),
                      "kernel": "attn_kernel (sink+window attention, one pass)",
-                     "flop_per_launch": r["attn_flops"], "avg_launch_ms": r["attn_ms"]},
+                     "flop_per_launch": r["attn_flops"], "avg_launch_ms": r["attn_ms"],
+                     "median_launch_ms": r["attn_ms_stats"]["median"], "sclk": r["sclk"]},
         "attn_tflops": r["attn_tflops"],
         "components": components,
     }
     if not args.no_cpu_baseline:
+        print("# cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
 

@@ -64,8 +64,29 @@ def test_traffic_summary_is_consistent():
 
 def test_cpu_baseline_small_workload():
     cfg = configs.Workload(**{**configs.TOY.__dict__, "passes": 1})
-    r = bench.cpu_baseline(cfg)
+    r = bench.cpu_baseline(cfg, full=False)
     assert r["kind"] == "oracle"
     assert r["unit"] == "latent frames/s per layer"
     assert r["value"] > 0 and r["seconds"] > 0 and r["cores"] >= 1
     assert "1 passes" in r["sample"]
+    assert r["extrapolated"] is False and r["cpu_model"]
+
+
+def test_append_bytes_count_scales_for_low_bit_caches():
+    rows = 3 * 1560 * 12
+    assert bench._append_bytes(rows, 128, "bf16") == 4 * rows * 128 * 2
+    for kv in ("int8", "fp8"):   # codes plus one fp32 scale per (token, head) row, K and V
+        assert bench._append_bytes(rows, 128, kv) == 2 * rows * 128 * 2 + 2 * rows * 128 + 2 * rows * 4
+
+
+def test_stats_percentiles():
+    st = bench._stats([float(x) for x in range(1, 101)])
+    assert st["median"] == 50.5 and st["min"] == 1.0 and st["n"] == 100
+    assert abs(st["p10"] - 10.9) < 1e-9 and abs(st["p90"] - 90.1) < 1e-9
+
+
+def test_clock_sampler_reports_rather_than_raises():
+    with bench.ClockSampler() as clk:
+        pass
+    s = clk.summary()
+    assert ("median_mhz" in s) or ("error" in s)
