@@ -3,7 +3,8 @@
     python -m streaming_kv_cache_block_amd.build
 
 Compiles every HIP source with hipcc for gfx950 into objects under ``_build/`` and
-links ``streaming_kv_cache_block_amd/libllcache.so``.  Packed-FP32 instruction
+links ``streaming_kv_cache_block_amd/libllcache.so``; also builds the seeded input
+generator's device twin ``synth/libsynthfill.so`` (input preparation, not the product).  Packed-FP32 instruction
 selection is switched off for device code.  ``slots_cli`` is built with g++ and
 the host sanitizers (it has no device code).
 """
@@ -23,6 +24,9 @@ SLOTS_CLI = os.path.join(BUILD, "slots_cli")
 
 HIP_SOURCES = ["attn.hip", "kvwrite.hip", "gemm.hip", "cache.cpp"]
 ARCH = "gfx950"
+# seeded input generator's device twin (synth/): a library of its own, not the product
+SYNTH_SRC = os.path.join(ROOT, "synth", "csrc", "fill.hip")
+SYNTH_LIB = os.path.join(ROOT, "synth", "libsynthfill.so")
 
 
 def _hipcc():
@@ -61,8 +65,15 @@ def build(verbose: bool = False) -> str:
             print(out)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(4, len(HIP_SOURCES))) as ex:
+    def synth_lib():
+        tmp = SYNTH_LIB + ".tmp"
+        _run([hipcc, "-x", "hip", *HIP_FLAGS, "-shared", SYNTH_SRC, "-o", tmp])
+        os.replace(tmp, SYNTH_LIB)
+
+    with ThreadPoolExecutor(max_workers=min(5, len(HIP_SOURCES) + 1)) as ex:
+        synth_job = ex.submit(synth_lib)
         objs = list(ex.map(compile_one, HIP_SOURCES))
+        synth_job.result()
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -8,10 +8,11 @@ the same bytes produced here.
 * ``normal_bf16`` draws on the host with numpy's Philox4x32-10 bit generator
   (Salmon et al., SC'11), keyed by a tuple of integers (seed, tensor id,
   layer, chunk, pass, ...).  Reproducible on any machine.
-* ``normal_bf16_device`` draws on the GPU with torch's device generator
-  seeded from the same key; used where host generation would be too slow
-  (30-layer rollouts).  The tests download those tensors when the oracle
-  needs them; nothing is regenerated on the host.
+* ``normal_bf16_device`` draws on the GPU with the counter-based generator of
+  ``synth.philox`` (Philox4x32-10 and a normal-quantile table) through its
+  device twin ``libsynthfill.so``; ``normal_bf16_philox`` draws the same bits
+  on the host, so any device draw can be regenerated from its key.  Used where
+  host generation would be too slow (30-layer rollouts, bench inputs).
 """
 
 import hashlib
@@ -51,15 +52,18 @@ def normal_bf16(shape, sigma, *key) -> np.ndarray:
     return f32_to_bf16_bits(normal_f32(shape, sigma, *key))
 
 
+def normal_bf16_philox(shape, sigma, *key) -> np.ndarray:
+    """bf16 bits (uint16) of the counter-based generator's N(0, sigma^2) draws for key
+    (the host twin of normal_bf16_device: the same bits)."""
+    from . import philox
+    return philox.normal_bf16(shape, sigma, key64(*key))
+
+
 def normal_bf16_device(shape, sigma, *key, device="cuda"):
-    """torch.bfloat16 tensor of N(0, sigma^2) drawn by the device generator."""
-    import torch
-    g = torch.Generator(device=device)
-    g.manual_seed(key64(*key))
-    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    if sigma != 1.0:
-        t.mul_(float(sigma))
-    return t.to(torch.bfloat16)
+    """torch.bfloat16 tensor of N(0, sigma^2) drawn on the device by the counter-based
+    generator (bit-identical to normal_bf16_philox of the same key)."""
+    from . import device as _dev
+    return _dev.fill_normal_bf16(shape, sigma, key64(*key), device)
 
 
 def to_device(bits, device="cuda"):
