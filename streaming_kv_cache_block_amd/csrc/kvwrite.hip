@@ -27,7 +27,8 @@ namespace ll {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;   // 16-byte vectors in flight per thread
+constexpr int kUnroll = 4;      // 16-byte vectors in flight per thread (copies)
+constexpr int kQuantRows = 2;   // rows per lane group of the quantising writes
 
 // grid: x = block within the frame, y = plan entry, z = 0 (K) / 1 (V)
 __global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams p, int64_t vecs_per_frame) {
@@ -49,22 +50,68 @@ __global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams
   }
 }
 
-// One (token, head) row of D values per LPR = D / 8 lanes; each lane owns 8 values of
-// RPG rows, whose loads are all issued before any arithmetic (bytes in flight).
+// Correctly rounded 1/a for a bf16 value a (8-bit significand) in the normal range: the
+// hardware reciprocal (within 1 ulp) and one Newton step with FMAs.  The step leaves a
+// relative error below 2^-45, and 1/a for an 8-bit significand lies at least 2^-25
+// (relative) away from any midpoint between binary32 neighbours (or is exact), so the
+// final rounding gives RN(1/a).  (Checked on gfx950 against IEEE division for every bf16
+// absmax in [2^-100, 2^120].)
+__device__ __forceinline__ float rcp_rn_bf16(float a) {
+  const float y0 = __builtin_amdgcn_rcpf(a);
+  const float e = __builtin_fmaf(-a, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
+// RN(a / M) by Markstein's correction with the constant RN(1/M) (valid without overflow
+// or underflow; the same check as above).
+template <int FMT>
+__device__ __forceinline__ float div_by_M(float a) {
+  constexpr float M = FMT == kKvFp8 ? 448.0f : 127.0f;
+  constexpr float yM = 1.0f / M;
+  const float q0 = a * yM;
+  const float r = __builtin_fmaf(-M, q0, a);
+  return __builtin_fmaf(r, yM, q0);
+}
+
+// Max over the LPR (8 or 16) lanes of a row, every lane ends with it: DPP inside quads
+// (xor 1, xor 2), then the half-row (8 lanes) and row (16 lanes) mirrors.
+template <int LPR>
+__device__ __forceinline__ float row_max(float v) {
+  auto dpp = [](float x, int ctrl) __attribute__((always_inline)) {
+    switch (ctrl) {
+      case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+      case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  static_assert(LPR == 8 || LPR == 16, "rows of 8 or 16 lanes");
+  v = fmaxf(v, dpp(v, 0xB1));
+  v = fmaxf(v, dpp(v, 0x4E));
+  v = fmaxf(v, dpp(v, 0x141));
+  if constexpr (LPR == 16) v = fmaxf(v, dpp(v, 0x140));
+  return v;
+}
+
+// One (token, head) row of D values per LPR = D / 8 lanes (aligned to DPP rows); each
+// lane owns 8 values of RPG rows, whose loads are all issued before any arithmetic.
 //
-// Division: q = rint(n / a) with n = x * 127 needs the correctly rounded quotient.  With
-// y = RN(1/a) (one IEEE division per row) and q0 = RN(n * y) within one ulp of n/a, the
-// residual r = n - a * q0 is exact as one FMA and RN(q0 + r * y) is the correctly rounded
-// n/a (Markstein's theorem for floating-point division, e.g. J.-M. Muller et al.,
-// Handbook of Floating-Point Arithmetic, ch. on division).  It needs no underflow or
-// overflow, so rows whose absmax is below 2^-100 or above 2^120 (where x * 127 may
-// overflow) use the plain IEEE division.
+// Division: q = rint(n / a) with n = x * M needs the correctly rounded quotient.  With
+// y = RN(1/a) and q0 = RN(n * y) within one ulp of n/a, the residual r = n - a * q0 is
+// exact as one FMA and RN(q0 + r * y) is the correctly rounded n/a (Markstein's theorem
+// for floating-point division, e.g. J.-M. Muller et al., Handbook of Floating-Point
+// Arithmetic, ch. on division).  It needs no underflow or overflow, so rows whose
+// absmax is below 2^-100 or above 2^120 (where x * M may overflow) take plain IEEE
+// divisions and the clamp; everywhere else |n / a| <= M holds exactly.
+// int8 codes: |q| <= 127, so q + 1.5 * 2^23 lies in [2^23, 2^24), where the spacing of
+// binary32 is 1: that one addition rounds q to the nearest integer, ties to even (rint),
+// and leaves it in the low byte of the sum's bits as a two's-complement byte.
 template <int D, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParams p) {
   constexpr float M = FMT == kKvFp8 ? 448.0f : 127.0f;
   constexpr int LPR = D / 8;
   constexpr int GROUPS = kThreads / LPR;
-  constexpr int RPG = 4;
+  constexpr int RPG = kQuantRows;
   const int e = blockIdx.y;
   const bool isv = blockIdx.z != 0;
   const int sub = threadIdx.x % LPR;
@@ -92,20 +139,20 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
     float a = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, LPR));
+    a = row_max<LPR>(a);
 
-    const float scale = a / M;
+    float scale = 0.0f;
     uint32_t packed[2] = {0u, 0u};
     if (a > 0.0f) {
       const bool plain = a < 0x1p-100f || a > 0x1p+120f;
-      const float y = 1.0f / a;
+      scale = plain ? a / M : div_by_M<FMT>(a);
+      const float y = plain ? 1.0f / a : rcp_rn_bf16(a);
       float qq[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float n = x[k] * M;   // exact for bf16 x
+        const float n = x[k] * M;   // exact for bf16 x unless it overflows
         if (plain) {
-          qq[k] = n / a;
+          qq[k] = fminf(fmaxf(n / a, -M), M);
         } else {
           qq[k] = n * y;
           const float r = __builtin_fmaf(-a, qq[k], n);
@@ -113,27 +160,24 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
         }
       }
       if constexpr (FMT == kKvFp8) {
-        // |quotient| <= 448 except when x * 448 overflowed (inf): saturate like the clamp.
         // The FMA correction turns a -0 quotient into +0; the IEEE quotient has the sign
         // of x (a > 0), and E4M3 keeps the sign of zero.
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qq[k] = __builtin_copysignf(fminf(fmaxf(qq[k], -448.0f), 448.0f), x[k]);
+        for (int k = 0; k < 8; ++k) qq[k] = __builtin_copysignf(qq[k], x[k]);
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          packed[w] = f32x2_to_e4m3x2(qq[4 * w], qq[4 * w + 1], 0u, false);
-          packed[w] = f32x2_to_e4m3x2(qq[4 * w + 2], qq[4 * w + 3], packed[w], true);
+        for (int w2 = 0; w2 < 2; ++w2) {
+          packed[w2] = f32x2_to_e4m3x2(qq[4 * w2], qq[4 * w2 + 1], 0u, false);
+          packed[w2] = f32x2_to_e4m3x2(qq[4 * w2 + 2], qq[4 * w2 + 3], packed[w2], true);
         }
       } else {
-        // q = clamp(rint(quotient), -127, 127) is an integer, so q + 128 in [1, 255] is
-        // exact and converts exactly to an unsigned byte; flipping bit 7 of each byte
-        // then gives the two's-complement code of q.
+        uint32_t t[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float t = __builtin_amdgcn_fmed3f(__builtin_rintf(qq[k]), -127.0f, 127.0f) + 128.0f;
-          packed[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(t, k & 3, packed[k >> 2]);
-        }
-        packed[0] ^= 0x80808080u;
-        packed[1] ^= 0x80808080u;
+        for (int k = 0; k < 8; ++k) t[k] = __builtin_bit_cast(uint32_t, qq[k] + 12582912.0f);
+        // low bytes of t[4j .. 4j+3] -> bytes 0..3 of one word
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          packed[j] = __builtin_amdgcn_perm(t[4 * j + 1], t[4 * j], 0x0c0c0400u) |
+                      __builtin_amdgcn_perm(t[4 * j + 3], t[4 * j + 2], 0x04000c0cu);
       }
     }
     if (row < p.rows_per_frame) {
@@ -154,7 +198,7 @@ hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t 
     hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kThreads), 0, s, p, vecs);
     return hipGetLastError();
   }
-  const int rows_per_block = kThreads / (D / 8) * 4;
+  const int rows_per_block = kThreads / (D / 8) * kQuantRows;
   dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
   if (D == 128 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<128, kKvInt8>), grid, dim3(kThreads), 0, s, p);
   else if (D == 64 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<64, kKvInt8>), grid, dim3(kThreads), 0, s, p);
