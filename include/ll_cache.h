@@ -33,6 +33,18 @@
  *     an error (no device, launch failure).  ll_last_error() gives text for the
  *     last failure on the calling thread.  Device faults of enqueued work are
  *     reported by the HIP runtime at a later synchronisation.
+ *
+ * Debug build (libllcache_debug.so: same kernels and interface, host side compiled
+ * with LL_DEBUG), for finding slot bookkeeping mistakes:
+ *   - every slot of a new cache is filled with NaN (bf16 caches: NaN values;
+ *     int8 / fp8 caches: NaN per-row scales), and a recache or window-only recache
+ *     fills the slots it rewrites with NaN before writing them, so a slot read
+ *     before a frame reached it turns the output into NaN;
+ *   - an attention call whose visible slots include one that holds no frame fails
+ *     with LL_ERR_STATE before launching anything;
+ *   - the slot planners check their internal invariants and abort the process on a
+ *     violation (the one case where an abort leaves the library).
+ *   Results of calls that pass these checks are bit-identical to the normal build.
  */
 #ifndef LL_CACHE_H
 #define LL_CACHE_H

@@ -20,6 +20,10 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllcache.so")
+# the same library with its host side built with LL_DEBUG: slots start as NaN and are
+# poisoned again before a rewrite, slot arithmetic bounds-checked, attention refuses to
+# walk a slot no frame was written to (Cache(..., debug=True))
+LIB_DEBUG_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllcache_debug.so")
 
 LL_OK, LL_ERR_INVALID, LL_ERR_OOM, LL_ERR_STATE, LL_ERR_HIP = range(5)
 LL_KV_BF16, LL_KV_INT8, LL_KV_FP8 = 0, 1, 2
@@ -33,7 +37,7 @@ EXPORTS = [
     "ll_cache_slot_frames", "ll_cache_slot_view", "ll_last_error",
 ]
 
-_lib = None
+_libs = {}
 
 
 class LLError(RuntimeError):
@@ -43,15 +47,15 @@ class LLError(RuntimeError):
         self.message = message
 
 
-def lib():
-    """Load libllcache.so (raises if it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+def lib(debug=False):
+    """Load libllcache.so, or its debug build (raises if it has not been built)."""
+    if debug in _libs:
+        return _libs[debug]
+    path = LIB_DEBUG_PATH if debug else LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m streaming_kv_cache_block_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i32, i64p = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)
     sig = {
         "ll_cache_create": [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(vp)],
@@ -76,13 +80,13 @@ def lib():
         f = getattr(L, name)
         f.argtypes = args
         f.restype = None if name == "ll_cache_destroy" else (ctypes.c_char_p if name == "ll_last_error" else i32)
-    _lib = L
+    _libs[debug] = L
     return L
 
 
-def _check(status):
+def _check(status, L=None):
     if status != LL_OK:
-        raise LLError(status, lib().ll_last_error().decode())
+        raise LLError(status, (L or lib()).ll_last_error().decode())
 
 
 def _ptr(x):
@@ -113,7 +117,9 @@ def _stream(stream):
 class Cache:
     """Per-layer sink + window KV cache living in device memory."""
 
-    def __init__(self, layers, heads, head_dim, tokens_per_frame, sink, window, kv_dtype="bf16", shot_sink=0):
+    def __init__(self, layers, heads, head_dim, tokens_per_frame, sink, window, kv_dtype="bf16", shot_sink=0,
+                 debug=False):
+        self._L = lib(debug)
         self.layers, self.heads, self.head_dim = layers, heads, head_dim
         self.T, self.S, self.W, self.Ss = tokens_per_frame, sink, window, shot_sink
         self.kv_dtype = kv_dtype
@@ -122,13 +128,13 @@ class Cache:
         dt = _KV_NAMES.get(kv_dtype, kv_dtype)
         self.kv_code = dt
         h = ctypes.c_void_p()
-        _check(lib().ll_cache_create_shots(layers, heads, head_dim, tokens_per_frame, sink, shot_sink, window, dt,
-                                           ctypes.byref(h)))
+        _check(self._L.ll_cache_create_shots(layers, heads, head_dim, tokens_per_frame, sink, shot_sink, window, dt,
+                                           ctypes.byref(h)), self._L)
         self._h = h
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
-            lib().ll_cache_destroy(self._h)
+            self._L.ll_cache_destroy(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):
@@ -160,15 +166,15 @@ class Cache:
 
     def append(self, layer, K, V, n_frames=None, stream=None):
         n = self._tokens(self._frames(K, n_frames), K=K, V=V)
-        _check(lib().ll_cache_append(self._h, layer, _ptr(K), _ptr(V), n, _stream(stream)))
+        _check(self._L.ll_cache_append(self._h, layer, _ptr(K), _ptr(V), n, _stream(stream)), self._L)
 
     def attn(self, layer, Q, K_chunk, V_chunk, out=None, n_frames=None, stream=None):
         if out is None:
             import torch
             out = torch.empty_like(Q)
         n = self._tokens(self._frames(Q, n_frames), Q=Q, K_chunk=K_chunk, V_chunk=V_chunk, out=out)
-        _check(lib().ll_attn_sink_window(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n, _ptr(out),
-                                         _stream(stream)))
+        _check(self._L.ll_attn_sink_window(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n, _ptr(out),
+                                         _stream(stream)), self._L)
         return out
 
     def attn_noalloc(self, layer, Q, K_chunk, V_chunk, out, n_frames=None, stream=None):
@@ -176,17 +182,17 @@ class Cache:
         scratch instead of the layer's work area (out must be given: nothing is
         allocated)."""
         n = self._tokens(self._frames(Q, n_frames), Q=Q, K_chunk=K_chunk, V_chunk=V_chunk, out=out)
-        _check(lib().ll_attn_sink_window_noalloc(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n,
-                                                 _ptr(out), _stream(stream)))
+        _check(self._L.ll_attn_sink_window_noalloc(self._h, layer, _ptr(Q), _ptr(K_chunk), _ptr(V_chunk), n,
+                                                 _ptr(out), _stream(stream)), self._L)
         return out
 
     def recache(self, layer, K_all, V_all, n_frames=None, stream=None):
         n = self._tokens(self._frames(K_all, n_frames), K_all=K_all, V_all=V_all)
-        _check(lib().ll_cache_recache(self._h, layer, _ptr(K_all), _ptr(V_all), n, _stream(stream)))
+        _check(self._L.ll_cache_recache(self._h, layer, _ptr(K_all), _ptr(V_all), n, _stream(stream)), self._L)
 
     def recache_window(self, layer, K_win, V_win, n_frames=None, stream=None):
         n = self._tokens(self._frames(K_win, n_frames), K_win=K_win, V_win=V_win)
-        _check(lib().ll_cache_recache_window(self._h, layer, _ptr(K_win), _ptr(V_win), n, _stream(stream)))
+        _check(self._L.ll_cache_recache_window(self._h, layer, _ptr(K_win), _ptr(V_win), n, _stream(stream)), self._L)
 
     def recache_from_hidden(self, layer, h, W_K, W_V, n_frames=None, stream=None):
         """Recache from hidden states h [n_frames*T][d_in]: K/V = h W^T written into the slots."""
@@ -198,31 +204,31 @@ class Cache:
         for name, w in (("W_K", W_K), ("W_V", W_V)):
             if w.numel() != d_out * d_in:
                 raise ValueError(f"{name} must be [{d_out}][{d_in}], got {tuple(w.shape)}")
-        _check(lib().ll_cache_recache_from_hidden(self._h, layer, _ptr(h), _ptr(W_K), _ptr(W_V), n, d_in,
-                                                  _stream(stream)))
+        _check(self._L.ll_cache_recache_from_hidden(self._h, layer, _ptr(h), _ptr(W_K), _ptr(W_V), n, d_in,
+                                                  _stream(stream)), self._L)
 
     def begin_shot(self, layer):
-        _check(lib().ll_cache_begin_shot(self._h, layer))
+        _check(self._L.ll_cache_begin_shot(self._h, layer), self._L)
 
     def shot_start(self, layer):
         v = ctypes.c_int64()
-        _check(lib().ll_cache_shot_start(self._h, layer, ctypes.byref(v)))
+        _check(self._L.ll_cache_shot_start(self._h, layer, ctypes.byref(v)), self._L)
         return v.value
 
     def frames_seen(self, layer):
         v = ctypes.c_int64()
-        _check(lib().ll_cache_frames_seen(self._h, layer, ctypes.byref(v)))
+        _check(self._L.ll_cache_frames_seen(self._h, layer, ctypes.byref(v)), self._L)
         return v.value
 
     def slot_frames(self, layer):
         arr = (ctypes.c_int64 * (self.S + self.Ss + self.W))()
-        _check(lib().ll_cache_slot_frames(self._h, layer, arr))
+        _check(self._L.ll_cache_slot_frames(self._h, layer, arr), self._L)
         return list(arr)
 
     def slot_view(self, layer):
         """(K, V, K_scale, V_scale) device pointers of the layer's slot arrays."""
         ptrs = [ctypes.c_void_p() for _ in range(4)]
-        _check(lib().ll_cache_slot_view(self._h, layer, *[ctypes.byref(p) for p in ptrs]))
+        _check(self._L.ll_cache_slot_view(self._h, layer, *[ctypes.byref(p) for p in ptrs]), self._L)
         return tuple(p.value for p in ptrs)
 
     def slot_bytes(self, layer):

@@ -20,6 +20,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libllcache.so")
+# debug library: the same kernels, the host side built with LL_DEBUG (NaN-poisoned slots,
+# bounds checks of the slot arithmetic, a check that attention walks only written slots)
+LIB_DEBUG = os.path.join(PKG, "libllcache_debug.so")
 SLOTS_CLI = os.path.join(BUILD, "slots_cli")
 
 HIP_SOURCES = ["attn.hip", "kvwrite.hip", "gemm.hip", "cache.cpp"]
@@ -70,13 +73,21 @@ def build(verbose: bool = False) -> str:
         _run([hipcc, "-x", "hip", *HIP_FLAGS, "-shared", SYNTH_SRC, "-o", tmp])
         os.replace(tmp, SYNTH_LIB)
 
-    with ThreadPoolExecutor(max_workers=min(5, len(HIP_SOURCES) + 1)) as ex:
+    def compile_debug_host():
+        obj = os.path.join(BUILD, "cache_debug.o")
+        _run([hipcc, "-x", "hip", *HIP_FLAGS, "-DLL_DEBUG", "-c", os.path.join(CSRC, "cache.cpp"), "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(6, len(HIP_SOURCES) + 2)) as ex:
         synth_job = ex.submit(synth_lib)
+        debug_job = ex.submit(compile_debug_host)
         objs = list(ex.map(compile_one, HIP_SOURCES))
         synth_job.result()
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+        debug_obj = debug_job.result()
+    for target, host in ((LIB, objs[-1]), (LIB_DEBUG, debug_obj)):
+        tmp = target + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs[:-1], host])
+        os.replace(tmp, target)
     build_slots_cli()
     return LIB
 

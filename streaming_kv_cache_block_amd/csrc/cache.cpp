@@ -158,6 +158,12 @@ ll_status attn_params(ll_cache* c, int layer, const void* Q, const void* K_chunk
   LL_TRY(check_device(c));
   const int64_t f0 = c->f0[size_t(layer)];
   const std::vector<ll::SlotRun> runs = ll::cache_runs(f0, c->layout(), c->fs[size_t(layer)]);
+#ifdef LL_DEBUG
+  for (const ll::SlotRun& r : runs)
+    for (int sl = r.first; sl < r.first + r.count; ++sl)
+      if (c->slot_frame[size_t(layer)][size_t(sl)] < 0)
+        return fail(LL_ERR_STATE, "debug check: attention of layer %d would read empty slot %d", layer, sl);
+#endif
   ll::AttnParams& p = *pp;
   p.Q = static_cast<const uint16_t*>(Q);
   p.Kc = static_cast<const uint16_t*>(K_chunk);
@@ -236,6 +242,46 @@ ll_status scratch_on_device(int dev, hipStream_t s, float** out) {
   return LL_OK;
 }
 
+#ifdef LL_DEBUG
+// Debug library: every slot starts poisoned (bf16 quiet NaN; for int8 / fp8 caches NaN
+// scales, so every dequantised value is NaN) and the slots a recache rewrites are
+// poisoned again just before, so an attention that reads a slot nobody wrote, or a
+// rewrite that misses a slot, shows up as NaN in the outputs or the slot bytes.  Internal
+// invariants of the slot arithmetic abort (slots.h, LL_CHECK): a library bug, not a
+// caller error.
+__global__ void poison_kernel(uint32_t* p, int64_t n_words, uint32_t pattern) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = pattern;
+}
+
+hipError_t poison(void* p, size_t bytes, uint32_t pattern, hipStream_t s) {
+  const int64_t words = int64_t(bytes / 4);
+  if (words == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((words + 255) / 256, 4096);
+  hipLaunchKernelGGL(poison_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, static_cast<uint32_t*>(p), words, pattern);
+  return hipGetLastError();
+}
+
+// Poison the slots of `layer` that the plan is about to write.
+ll_status poison_planned(ll_cache* c, int layer, const std::vector<ll::WriteEntry>& plan, hipStream_t s) {
+  const size_t slot_vals = size_t(c->rows_per_frame) * size_t(c->head_dim);
+  for (const ll::WriteEntry& w : plan) {
+    hipError_t e;
+    if (c->kv_dtype == LL_KV_BF16) {
+      e = poison(static_cast<char*>(c->k(layer)) + size_t(w.slot) * slot_vals * 2, slot_vals * 2, 0x7FC07FC0u, s);
+      if (e == hipSuccess)
+        e = poison(static_cast<char*>(c->v(layer)) + size_t(w.slot) * slot_vals * 2, slot_vals * 2, 0x7FC07FC0u, s);
+    } else {
+      e = poison(c->ks(layer) + size_t(w.slot) * size_t(c->rows_per_frame), size_t(c->rows_per_frame) * 4, 0x7FC00000u, s);
+      if (e == hipSuccess)
+        e = poison(c->vs(layer) + size_t(w.slot) * size_t(c->rows_per_frame), size_t(c->rows_per_frame) * 4, 0x7FC00000u, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "poisoning slots before a rewrite");
+  }
+  return LL_OK;
+}
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -300,6 +346,13 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
   e = hipStreamCreateWithFlags(&zs, hipStreamNonBlocking);
   if (e == hipSuccess) {
     e = hipMemsetAsync(static_cast<char*>(mem) + cnt_offset, 0, size_t(layers) * size_t(cnt_layer_bytes), zs);
+#ifdef LL_DEBUG
+    if (e == hipSuccess) {   // every slot poisoned: bf16 NaN codes, or NaN scales
+      if (!quantised) e = poison(mem, size_t(layers) * 2 * size_t(kv_bytes), 0x7FC07FC0u, zs);
+      else e = poison(static_cast<char*>(mem) + size_t(layers) * 2 * size_t(kv_bytes), size_t(layers) * 2 * size_t(sc_bytes),
+                      0x7FC00000u, zs);
+    }
+#endif
     if (e == hipSuccess) {
       const ll_status st = scratch_on_device(dev, zs, nullptr);
       if (st != LL_OK) {
@@ -419,8 +472,11 @@ ll_status ll_cache_recache(ll_cache* c, int layer, const void* K_all, const void
                 (long long)need, n_frames);
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
-  LL_TRY(write_frames(c, layer, K_all, V_all, ll::recache_plan(f0, c->layout(), fs), static_cast<hipStream_t>(stream),
-                      "recache launch"));
+  const std::vector<ll::WriteEntry> plan = ll::recache_plan(f0, c->layout(), fs);
+#ifdef LL_DEBUG
+  LL_TRY(poison_planned(c, layer, plan, static_cast<hipStream_t>(stream)));
+#endif
+  LL_TRY(write_frames(c, layer, K_all, V_all, plan, static_cast<hipStream_t>(stream), "recache launch"));
   return ok();
 }
 
@@ -437,8 +493,11 @@ ll_status ll_cache_recache_window(ll_cache* c, int layer, const void* K_win, con
                 (long long)need, n_frames);
   LL_TRY(check_frames(c, n_frames));
   LL_TRY(check_device(c));
-  LL_TRY(write_frames(c, layer, K_win, V_win, ll::recache_window_plan(f0, c->layout(), c->fs[size_t(layer)]),
-                      static_cast<hipStream_t>(stream), "recache_window launch"));
+  const std::vector<ll::WriteEntry> plan = ll::recache_window_plan(f0, c->layout(), c->fs[size_t(layer)]);
+#ifdef LL_DEBUG
+  LL_TRY(poison_planned(c, layer, plan, static_cast<hipStream_t>(stream)));
+#endif
+  LL_TRY(write_frames(c, layer, K_win, V_win, plan, static_cast<hipStream_t>(stream), "recache_window launch"));
   return ok();
 }
 

@@ -41,6 +41,9 @@ def test_every_declared_symbol_is_exported(L):
     assert set(names) == set(ll.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
+    D = ll.lib(debug=True)           # the debug build exports the same interface
+    for n in names:
+        assert hasattr(D, n), n
 
 
 def test_create_rejects_invalid_arguments_before_touching_hip(L):
