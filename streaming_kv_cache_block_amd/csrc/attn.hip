@@ -16,9 +16,10 @@
 //   * K and V tiles live in LDS in their natural [key][d] layout, double-buffered,
 //     one barrier per tile.  16-byte chunks are XOR-swizzled per row so that the
 //     MFMA operand reads below are free of bank conflicts.  bf16 tiles are copied
-//     global -> LDS by the buffer load-to-LDS path (no registers); int8 / fp8 cache
-//     tiles are copied as codes into a per-wave staging area the same way and widened
-//     to bf16 by that wave (exact: |q| <= 127, and every E4M3 value is a bf16 value).
+//     global -> LDS by the buffer load-to-LDS path (no registers), one tile ahead;
+//     int8 / fp8 cache tiles are copied as codes (with their scales) into a staging
+//     area the same way, two tiles ahead, and each wave widens the rows it copied to
+//     bf16 while the score MFMAs of the tile before run.
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA: a
 //     lane then holds one query's scores for 16 keys of each 32-key block, so the
 //     running row max needs one register exchange with lane ^ 32
@@ -30,12 +31,14 @@
 //   * Online softmax in base 2, log2(e)/sqrt(D) folded into one FMA; the running
 //     max is only raised (and O, l rescaled) when a score exceeds it by more than
 //     2^8, which keeps every probability <= 256 and skips almost all rescales.
-//     Full bf16 tiles first take the probabilities against the running max as it
+//     Full tiles first take the probabilities against the running max as it
 //     stands and check the bound on the lane's tile sum; only tiles that fail it
 //     (rare after the first) compute the tile max, rescale and take them again.
-//   * int8 / fp8 caches: the per-key K scale multiplies the score column and the V
-//     scale the probability column before rounding to bf16 (LongLive-2.0 explainer,
-//     wmrh.cn, §15.3: dequantisation fused into the consumer, not a separate pass).
+//   * int8 / fp8 caches (LongLive-2.0 explainer, wmrh.cn, §15.3: dequantisation fused
+//     into the consumer, not a separate pass): the K codes enter the MFMAs as they are
+//     (exact in bf16) and the per-key factor K scale x log2(e)/sqrt(D) scales the score
+//     column in fp32; V is dequantised to bf16 (q * s, one rounding) when widened.
+//     Both then take the same speculative softmax as bf16 tiles.
 //   * Workgroups are numbered so that the query tiles of one head run on the same
 //     XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs) and share
 //     its L2 while they stream the same keys.
@@ -141,63 +144,97 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int64_t rs, int wave, int la
   return uint32_t((int64_t(r) * rs + 8 * swz<D>(r, lane % G::CH)) * 2);
 }
 
-// Quantised cache tile (int8 or fp8 codes): each wave copies whole rows of raw codes
-// into a staging area (load-to-LDS, natural [row][D bytes] layout) and, after its own
-// copies have landed, widens exactly those rows to bf16 in the swizzled tile buffer
-// (exact: |q| <= 127, and every E4M3 value is a bf16 value).
-// No wave reads another wave's staging rows, so no barrier is needed in between.  The
-// per-row scales are copied straight into their LDS arrays by waves 0 (K) and 1 (V).
+// Quantised cache tile (int8 or fp8 codes): each wave copies whole rows of raw codes,
+// and the K and V scales of those rows, into its part of a staging area (load-to-LDS,
+// natural [row][D bytes] layout); later, once its own copies have landed, it widens
+// exactly those rows into the swizzled bf16 tile buffers:
+//   K: the codes themselves (exact: |q| <= 127, and every E4M3 value is a bf16 value);
+//      the row's K scale times log2(e)/sqrt(D) goes to the tile's per-key factor
+//      array, applied to the score column in fp32 (the scores stay exact products of
+//      Q with the codes);
+//   V: the dequantised values q * s rounded to bf16 (LongLive-2.0 explainer, wmrh.cn,
+//      §15.3: dequantised where they are consumed), so the tile's P*V is the bf16 one.
+// No wave reads another wave's staging rows, so no barrier is needed in between.
 template <int D, int NW, int FMT>
 struct QTile {
   static constexpr int CH8 = D / 16;                 // 16-byte chunks per int8 row
   static constexpr int ROWS = 64 / CH8;              // rows per wave-wide 1 KB copy
   static constexpr int COPIES = BN / ROWS;           // copies per operand per tile
-  static constexpr int STAGE = BN * D;               // bytes per operand
+  static constexpr int ITER = COPIES / NW;           // copies per wave
+  static constexpr int STAGE = BN * D;               // code bytes per operand
+  static constexpr int SCALES = NW * ITER * 128;     // staged scales (floats): K, V per copy
+  static constexpr int OPS = 4 * ITER;               // vector-memory instructions of issue()
+  static_assert(COPIES % NW == 0 && ROWS <= 64, "every wave copies the same number of rows");
 
-  __device__ static void issue(const AttnParams& p, int h, const TileInfo& ti, int8_t* stage, float* lks,
-                               float* lvs, int wave, int lane) {
+  __device__ static void issue(const AttnParams& p, int h, const TileInfo& ti, int8_t* stage, float* sst,
+                               int wave, int lane) {
     const int64_t rs = int64_t(p.H) * D;
     const int8_t* gk = static_cast<const int8_t*>(p.cK) + int64_t(h) * D;
     const int8_t* gv = static_cast<const int8_t*>(p.cV) + int64_t(h) * D;
-    for (int i = wave; i < COPIES; i += NW) {
+    const int64_t base = int64_t(ti.start) * rs;
+    const int64_t sbase = int64_t(ti.start) * p.H + h;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int i = wave + it * NW;
       const int r0 = i * ROWS;
-      const int r = r0 + lane / CH8;
-      const int64_t base = int64_t(ti.start) * rs;
-      const uint32_t off = uint32_t(int64_t(min(r, ti.cnt - 1)) * rs + 16 * (lane % CH8));
+      // rows past the end re-read the last one (masked to -inf, finite data)
+      const uint32_t off = uint32_t(int64_t(min(r0 + lane / CH8, ti.cnt - 1)) * rs + 16 * (lane % CH8));
       copy_lds<16>(gk + base, off, stage + r0 * D);
       copy_lds<16>(gv + base, off, stage + STAGE + r0 * D);
-    }
-    if (wave < 2) {
-      const float* sp = (wave == 0 ? p.cKs : p.cVs) + int64_t(ti.start) * p.H + h;
-      copy_lds<4>(sp, uint32_t(min(lane, ti.cnt - 1) * p.H * 4), wave == 0 ? lks : lvs);
+      // scales: lane t of the copy takes row r0 + t % ROWS
+      const uint32_t soff = uint32_t(min(r0 + lane % ROWS, ti.cnt - 1) * p.H * 4);
+      float* dst = sst + (wave * ITER + it) * 128;
+      copy_lds<4>(p.cKs + sbase, soff, dst);
+      copy_lds<4>(p.cVs + sbase, soff, dst + 64);
     }
   }
 
-  // Called by the same wave after s_waitcnt vmcnt(0).
-  __device__ static void widen(const int8_t* stage, uint16_t* lk, uint16_t* lv, int wave, int lane) {
-    for (int i = wave; i < COPIES; i += NW) {
+  // Called by the same wave once its copies of the tile have landed.  c = log2(e)/sqrt(D).
+  __device__ static void widen(const int8_t* stage, const float* sst, uint16_t* lk, uint16_t* lv, float* lkf,
+                               float c, int wave, int lane) {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int i = wave + it * NW;
       const int r = i * ROWS + lane / CH8;
       const int c16 = lane % CH8;
-#pragma unroll
-      for (int op = 0; op < 2; ++op) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(stage + op * STAGE + i * ROWS * D + 16 * lane);
-        uint16_t* dst = op ? lv : lk;
-        *reinterpret_cast<u32x4*>(dst + r * D + 8 * swz<D>(r, 2 * c16)) =
-            u32x4{code2_to_bf16x2<FMT>(q.x, 0), code2_to_bf16x2<FMT>(q.x, 2), code2_to_bf16x2<FMT>(q.y, 0),
-                  code2_to_bf16x2<FMT>(q.y, 2)};
-        *reinterpret_cast<u32x4*>(dst + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
-            u32x4{code2_to_bf16x2<FMT>(q.z, 0), code2_to_bf16x2<FMT>(q.z, 2), code2_to_bf16x2<FMT>(q.w, 0),
-                  code2_to_bf16x2<FMT>(q.w, 2)};
-      }
+      const u32x4 qk = *reinterpret_cast<const u32x4*>(stage + i * ROWS * D + 16 * lane);
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(stage + STAGE + i * ROWS * D + 16 * lane);
+      const float* sc = sst + (wave * ITER + it) * 128 + lane / CH8;
+      const float sk = sc[0], sv = sc[64];
+      *reinterpret_cast<u32x4*>(lk + r * D + 8 * swz<D>(r, 2 * c16)) =
+          u32x4{code2_to_bf16x2<FMT>(qk.x, 0), code2_to_bf16x2<FMT>(qk.x, 2), code2_to_bf16x2<FMT>(qk.y, 0),
+                code2_to_bf16x2<FMT>(qk.y, 2)};
+      *reinterpret_cast<u32x4*>(lk + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
+          u32x4{code2_to_bf16x2<FMT>(qk.z, 0), code2_to_bf16x2<FMT>(qk.z, 2), code2_to_bf16x2<FMT>(qk.w, 0),
+                code2_to_bf16x2<FMT>(qk.w, 2)};
+      *reinterpret_cast<u32x4*>(lv + r * D + 8 * swz<D>(r, 2 * c16)) =
+          u32x4{dequant2_bf16x2<FMT>(qv.x, 0, sv), dequant2_bf16x2<FMT>(qv.x, 2, sv),
+                dequant2_bf16x2<FMT>(qv.y, 0, sv), dequant2_bf16x2<FMT>(qv.y, 2, sv)};
+      *reinterpret_cast<u32x4*>(lv + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
+          u32x4{dequant2_bf16x2<FMT>(qv.z, 0, sv), dequant2_bf16x2<FMT>(qv.z, 2, sv),
+                dequant2_bf16x2<FMT>(qv.w, 0, sv), dequant2_bf16x2<FMT>(qv.w, 2, sv)};
+      if (c16 == 0) lkf[r] = sk * c;
     }
   }
 };
 
+// Wait until at most N vector-memory instructions of this wave are in flight (they
+// complete in issue order).
+// (The builtin, not inline asm: the compiler's own wait placement then knows what has
+// completed.)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // vmcnt(N), expcnt and lgkmcnt not waited for
+}
+
 // Order of the key tiles of a launch whose cached context is one run of rows (every
 // cache without a shot sink): the (at most two) partial tiles -- the last tile of the
 // run and of the own chunk -- come first, so that the long stretch of full tiles after
-// them carries no masking code; then the full cache tiles, then the full own-chunk
-// tiles.  Softmax attention does not depend on the order of its keys.
+// them carries no masking code; then the full own-chunk tiles, then the full cache
+// tiles (last, so that a quantised cache's tiles, which are staged two tiles ahead,
+// form one uninterrupted stretch to the end of the walk).  Softmax attention does not
+// depend on the order of its keys.
 struct TileOrder1 {
   int n1, n2, np1, np2, ncache, nq, r0;
   __device__ explicit TileOrder1(const AttnParams& p)
@@ -208,7 +245,7 @@ struct TileOrder1 {
     np2 = (nq % BN) != 0;
   }
   __device__ int npart() const { return np1 + np2; }
-  __device__ int full1_end() const { return np1 + np2 + n1 - np1; }   // end of the full cache tiles
+  __device__ int own_end() const { return np1 + np2 + nq / BN; }   // end of the full own-chunk tiles
   __device__ int total() const { return n1 + n2; }
   __device__ TileInfo at(int j) const {
     TileInfo t;
@@ -222,13 +259,13 @@ struct TileOrder1 {
         t.start = (n2 - 1) * BN;
         t.cnt = nq - t.start;
       }
-    } else if (j < full1_end()) {
-      t.seg = 0;
-      t.start = r0 + (j - np1 - np2) * BN;
+    } else if (j < own_end()) {
+      t.seg = 1;
+      t.start = (j - np1 - np2) * BN;
       t.cnt = BN;
     } else {
-      t.seg = 1;
-      t.start = (j - full1_end()) * BN;
+      t.seg = 0;
+      t.start = r0 + (j - own_end()) * BN;
       t.cnt = BN;
     }
     return t;
@@ -236,10 +273,11 @@ struct TileOrder1 {
 };
 
 // General order of the key tiles (a shot sink can split the cached context).  The keys
-// are the cached runs (up to kMaxRuns runs of rows of the slot array) and the own chunk; each is tiled on its own, so only the last tile of
-// each may be partial.  The partial tiles come first, so that the long stretch of full
-// tiles after them carries no masking code; then the full cache tiles run by run, then
-// the full own-chunk tiles.  Softmax attention does not depend on the order of its keys.
+// are the cached runs (up to kMaxRuns runs of rows of the slot array) and the own
+// chunk; each is tiled on its own, so only the last tile of each may be partial.  The
+// partial tiles come first, so that the long stretch of full tiles after them carries
+// no masking code; then the full own-chunk tiles, then the full cache tiles run by
+// run.  Softmax attention does not depend on the order of its keys.
 // (All loops are unrolled over the run count so the tables stay in scalar registers.)
 struct TileOrderN {
   int r0[kMaxRuns], rn[kMaxRuns], fc[kMaxRuns];   // first row, rows, full tiles per run
@@ -259,7 +297,7 @@ struct TileOrderN {
     if (nq % BN) ++np;
   }
   __device__ int npart() const { return np; }
-  __device__ int full1_end() const { return np + nfc; }   // end of the full cache tiles
+  __device__ int own_end() const { return np + nq / BN; }   // end of the full own-chunk tiles
   __device__ int total() const { return np + nfc + nq / BN; }
   __device__ TileInfo at(int j) const {
     TileInfo t;
@@ -278,8 +316,12 @@ struct TileOrderN {
           }
           ++seen;
         }
-    } else if (j < np + nfc) {
-      const int jj = j - np;
+    } else if (j < own_end()) {
+      t.seg = 1;
+      t.start = (j - np) * BN;
+      t.cnt = BN;
+    } else {
+      const int jj = j - own_end();
       t.seg = 0;
       t.start = 0;
       t.cnt = BN;
@@ -289,10 +331,6 @@ struct TileOrderN {
         if (jj >= base && jj < base + fc[k]) t.start = r0[k] + (jj - base) * BN;
         base += fc[k];
       }
-    } else {
-      t.seg = 1;
-      t.start = (j - np - nfc) * BN;
-      t.cnt = BN;
     }
     return t;
   }
@@ -326,35 +364,22 @@ struct Attn {
   }
 
   // S^T = K Q^T for the 64 keys of a tile (two 32-key blocks).  MASK: keys >= cnt get
-  // -inf; SCALED (int8 tile, when `scaled`): the per-key K scale multiplies its column.
+  // -inf; SCALED (quantised tile, when `scaled`): the column of key j is multiplied by
+  // its factor kf_j = K scale x log2(e)/sqrt(D), so the scores come out in log2 units.
   template <bool MASK, bool SCALED>
-  __device__ __forceinline__ void scores(const uint16_t* lk, const float* lks, int cnt, bool scaled,
+  __device__ __forceinline__ void scores(const uint16_t* lk, const float* lkf, int cnt, bool scaled,
                                          f32x16 (&S)[NQB][2]) const {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) S[qb][0] = S[qb][1] = f32x16{};
-    // Scaled (int8 / fp8) tiles: K fragments read two steps ahead of the MFMAs that use
-    // them.  (Measured: that pays on the scaled tiles; on bf16 tiles the compiler's own
-    // one-step order is faster.)
-    constexpr int kLook = (SCALED && !MASK) ? 2 : 1;
-    bf16x8 kf[kLook + 1][2];
-    auto kread = [&](int s, bf16x8 (&f)[2]) __attribute__((always_inline)) {
-      const int ko = kofs ^ (16 * s);
-      f[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + ko));
-      f[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + 32 * D + ko));
-    };
-    if constexpr (kLook > 1) {
-#pragma unroll
-      for (int s = 0; s < kLook; ++s) kread(s, kf[s]);
-    }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      if constexpr (kLook == 1) kread(s, kf[s & 1]);
-      else if (s + kLook < D / 16) kread(s + kLook, kf[(s + kLook) % (kLook + 1)]);
-      const bf16x8 (&f)[2] = kf[kLook == 1 ? (s & 1) : s % (kLook + 1)];
+      const int ko = kofs ^ (16 * s);
+      const bf16x8 f0 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + ko));
+      const bf16x8 f1 = as_bf16x8(*reinterpret_cast<const u32x4*>(lk + 32 * D + ko));
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        S[qb][0] = mfma32(f[0], qf[qb][s], S[qb][0]);
-        S[qb][1] = mfma32(f[1], qf[qb][s], S[qb][1]);
+        S[qb][0] = mfma32(f0, qf[qb][s], S[qb][0]);
+        S[qb][1] = mfma32(f1, qf[qb][s], S[qb][1]);
       }
     }
     if (SCALED && scaled) {
@@ -362,7 +387,7 @@ struct Attn {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 kscv = *reinterpret_cast<const f32x4*>(lks + 32 * b + 8 * i + 4 * g);
+          const f32x4 kscv = *reinterpret_cast<const f32x4*>(lkf + 32 * b + 8 * i + 4 * g);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -384,10 +409,13 @@ struct Attn {
   }
 
   // Online softmax of one tile (base 2, lazy rescale) -> bf16 probabilities in the
-  // B-operand layout of the P*V product.  SCALED: the per-key V scale multiplies P.
+  // B-operand layout of the P*V product.  Scores of a scaled tile are already in log2
+  // units (scores() applied the per-key factors); the others take log2(e)/sqrt(D) here.
+  // The row sum is taken over the bf16 probabilities that P*V uses (two per dot2), so
+  // the normalised weights sum to one exactly as applied.
   template <bool SCALED>
-  __device__ __forceinline__ void softmax(f32x16 (&S)[NQB][2], const float* lvs, bool scaled,
-                                          bf16x8 (&P)[NQB][4]) {
+  __device__ __forceinline__ void softmax(f32x16 (&S)[NQB][2], bool scaled, bf16x8 (&P)[NQB][4]) {
+    const float cc = (SCALED && scaled) ? 1.0f : c;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       float mx = S[qb][0][0];
@@ -397,7 +425,7 @@ struct Attn {
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[qb][b][v]);
       {  // lanes l and l ^ 32 hold the two halves of a query's keys: exchange in registers
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cc;
       }
       if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kLazyThreshold)) {
         const float mnew = fmaxf(m[qb], mx);
@@ -410,41 +438,21 @@ struct Attn {
       const float mq = m[qb];
       float rsum = 0.0f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          S[qb][b][v] = fast_exp2(__builtin_fmaf(S[qb][b][v], c, -mq));
-          if (SCALED && scaled) rsum += S[qb][b][v];
-        }
-      if (SCALED && scaled) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 vscv = *reinterpret_cast<const f32x4*>(lvs + 32 * b + 8 * i + 4 * g);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) S[qb][b][4 * i + jj] *= vscv[jj];
-          }
-      }
-      // Unscaled tiles: the row sum is taken over the bf16 probabilities that P*V uses
-      // (two per dot2), so the normalised weights sum to one exactly as applied.
-      // Scaled tiles sum the fp32 probabilities before the V scale (above).
-      const bool sum_packed = !(SCALED && scaled);
-#pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int b = u >> 1, v0 = 8 * (u & 1);
+        float e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) e[t] = fast_exp2(__builtin_fmaf(S[qb][b][v0 + t], cc, -mq));
         u32x4 w;
-        w.x = pack_bf16x2(S[qb][b][v0 + 0], S[qb][b][v0 + 1]);
-        w.y = pack_bf16x2(S[qb][b][v0 + 2], S[qb][b][v0 + 3]);
-        w.z = pack_bf16x2(S[qb][b][v0 + 4], S[qb][b][v0 + 5]);
-        w.w = pack_bf16x2(S[qb][b][v0 + 6], S[qb][b][v0 + 7]);
+        w.x = pack_bf16x2(e[0], e[1]);
+        w.y = pack_bf16x2(e[2], e[3]);
+        w.z = pack_bf16x2(e[4], e[5]);
+        w.w = pack_bf16x2(e[6], e[7]);
         P[qb][u] = as_bf16x8(w);
-        if (sum_packed) {
-          rsum = dot2_ones(w.x, rsum);
-          rsum = dot2_ones(w.y, rsum);
-          rsum = dot2_ones(w.z, rsum);
-          rsum = dot2_ones(w.w, rsum);
-        }
+        rsum = dot2_ones(w.x, rsum);
+        rsum = dot2_ones(w.y, rsum);
+        rsum = dot2_ones(w.z, rsum);
+        rsum = dot2_ones(w.w, rsum);
       }
       l[qb] += rsum;
     }
@@ -467,7 +475,7 @@ struct Attn {
   // ORDERED: the V^T fragments of key step u + 1 are read before the MFMAs of step u
   // are issued, an order pinned through the scheduler with sched_group_barrier (left
   // to itself it reads each fragment just before its MFMA and waits for it there).
-  // Used on the bf16 tiles; on the scaled tiles the extra live fragments cost more.
+  // Used on the full tiles.
   template <bool ORDERED>
   __device__ __forceinline__ void pv(const uint16_t* lv, const bf16x8 (&P)[NQB][4]) {
     if constexpr (ORDERED) {
@@ -507,17 +515,31 @@ struct Attn {
     }
   }
 
-  // Probabilities of a full unscaled tile against running max mq, packed to bf16 in
-  // the P*V operand layout; returns the lane's sum of the packed values (the weights
-  // P*V applies).
-  __device__ __forceinline__ float exp_pack(const f32x16 (&S)[2], float mq, bf16x8 (&P)[4]) const {
+  // Probabilities of a full tile against running max mq, packed to bf16 in the P*V
+  // operand layout; returns the lane's sum of the packed values (the weights P*V
+  // applies).  Score j takes the factor log2(e)/sqrt(D), or on a scaled tile its own
+  // factor kf_j, read from LDS just before use (the lane's keys of step u are
+  // 32 (u >> 1) + 16 (u & 1) + 8 (t >> 2) + 4 g + (t & 3), t = 0..7).
+  template <bool SCALED>
+  __device__ __forceinline__ float exp_pack(const f32x16 (&S)[2], float mq, const float* lkf,
+                                            bf16x8 (&P)[4]) const {
     float part[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int b = u >> 1, v0 = 8 * (u & 1);
       float e[8];
+      if constexpr (SCALED) {
+        const f32x4 f0 = *reinterpret_cast<const f32x4*>(lkf + 32 * b + 16 * (u & 1) + 4 * g);
+        const f32x4 f1 = *reinterpret_cast<const f32x4*>(lkf + 32 * b + 16 * (u & 1) + 8 + 4 * g);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) e[t] = fast_exp2(__builtin_fmaf(S[b][v0 + t], c, -mq));
+        for (int t = 0; t < 4; ++t) {
+          e[t] = fast_exp2(__builtin_fmaf(S[b][v0 + t], f0[t], -mq));
+          e[t + 4] = fast_exp2(__builtin_fmaf(S[b][v0 + 4 + t], f1[t], -mq));
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) e[t] = fast_exp2(__builtin_fmaf(S[b][v0 + t], c, -mq));
+      }
       u32x4 w;
       w.x = pack_bf16x2(e[0], e[1]);
       w.y = pack_bf16x2(e[2], e[3]);
@@ -529,25 +551,51 @@ struct Attn {
     return (part[0] + part[1]) + (part[2] + part[3]);
   }
 
-  // Full unscaled tile with the probabilities first taken against the running max as it
+  // Tile max of the scores in log2 units, over the lane pair of each query.
+  template <bool SCALED>
+  __device__ __forceinline__ float tile_max(const f32x16 (&S)[2], const float* lkf) const {
+    float mx = -__builtin_inff();
+    if constexpr (SCALED) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 f = *reinterpret_cast<const f32x4*>(lkf + 32 * b + 8 * i + 4 * g);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, S[b][4 * i + jj] * f[jj]);
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[b][v]);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    return SCALED ? mx : mx * c;
+  }
+
+  // Full tile with the probabilities first taken against the running max as it
   // stands.  They are non-negative, so all of a lane's probabilities are at most 2^8
   // exactly when its tile sum is; then the tile needs no new max (the same bound the
   // lazy rescale keeps).  Otherwise (a score more than 8 above the running max, or the
   // first tile of a walk, where the max is -inf) the scores are recomputed from the K
   // tile, still in LDS, the running max is raised to the tile's max and O and l are
   // rescaled before the probabilities are taken again.  The common case skips the
-  // per-tile max and its exchange between the two lanes of a query.  (Scaled int8 /
-  // fp8 tiles keep softmax(): there the extra scale work ate the gain.)
-  __device__ __forceinline__ void tile_spec(const uint16_t* lk, const uint16_t* lv) {
+  // per-tile max and its exchange between the two lanes of a query.  SCALED: a
+  // quantised cache tile (per-key factors kf_j in LDS, V already dequantised).
+  template <bool SCALED, class Mid>
+  __device__ __forceinline__ void tile_spec(const uint16_t* lk, const uint16_t* lv, const float* lkf, Mid&& mid) {
     constexpr float kBound = float(1 << int(kLazyThreshold));
     f32x16 S[NQB][2];
     bf16x8 P[NQB][4];
     scores<false, false>(lk, nullptr, BN, false, S);
+    mid();
     float rsum[NQB];
     bool over = false;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      rsum[qb] = exp_pack(S[qb], m[qb], P[qb]);
+      rsum[qb] = exp_pack<SCALED>(S[qb], m[qb], lkf, P[qb]);
       over |= !(rsum[qb] <= kBound);
     }
     if (__builtin_amdgcn_ballot_w64(over)) {
@@ -558,19 +606,13 @@ struct Attn {
       scores<false, false>(lk + z, nullptr, BN, false, S);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        float mx = S[qb][0][0];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[qb][b][v]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        const float mnew = fmaxf(m[qb], fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c);
+        const float mnew = fmaxf(m[qb], tile_max<SCALED>(S[qb], lkf));
         const float alpha = fast_exp2(m[qb] - mnew);
         m[qb] = mnew;
         l[qb] *= alpha;
 #pragma unroll
         for (int e = 0; e < D / 32; ++e) O[qb][e] *= alpha;
-        rsum[qb] = exp_pack(S[qb], mnew, P[qb]);
+        rsum[qb] = exp_pack<SCALED>(S[qb], mnew, lkf, P[qb]);
       }
     }
 #pragma unroll
@@ -578,17 +620,20 @@ struct Attn {
     pv<true>(lv, P);
   }
 
-  // One whole tile from LDS: scores, softmax, P*V.
-  template <bool MASK, bool SCALED>
-  __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lks, const float* lvs,
-                                       int cnt, bool scaled = SCALED) {
-    if constexpr (!MASK && !SCALED) {
-      tile_spec(lk, lv);
+  // One whole tile from LDS: scores, softmax, P*V.  Full tiles take the speculative
+  // path, partial tiles the masked one.  mid() runs once the score MFMAs are issued
+  // (independent work placed there executes beside them).
+  template <bool MASK, bool SCALED, class Mid>
+  __device__ __forceinline__ void tile(const uint16_t* lk, const uint16_t* lv, const float* lkf, int cnt,
+                                       bool scaled, Mid&& mid) {
+    if constexpr (!MASK) {
+      tile_spec<SCALED>(lk, lv, lkf, mid);
     } else {
       f32x16 S[NQB][2];
       bf16x8 P[NQB][4];
-      scores<MASK, SCALED>(lk, lks, cnt, scaled, S);
-      softmax<SCALED>(S, lvs, scaled, P);
+      scores<MASK, SCALED>(lk, lkf, cnt, scaled, S);
+      mid();
+      softmax<SCALED>(S, scaled, P);
       pv<false>(lv, P);
     }
   }
@@ -723,11 +768,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v0[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v1[G::TILE];
   constexpr bool KV8 = KVQ != kKvBf16;   // quantised cache (int8 or fp8 codes)
-  __shared__ __attribute__((aligned(16))) float sm_ks0[KV8 ? BN : 1];
-  __shared__ __attribute__((aligned(16))) float sm_ks1[KV8 ? BN : 1];
-  __shared__ __attribute__((aligned(16))) float sm_vs0[KV8 ? BN : 1];
-  __shared__ __attribute__((aligned(16))) float sm_vs1[KV8 ? BN : 1];
-  __shared__ __attribute__((aligned(1024))) int8_t sm_stage[KV8 ? 2 * QTile<D, NW, KVQ>::STAGE : 16];
+  using QT = QTile<D, NW, KVQ>;
+  __shared__ __attribute__((aligned(16))) float sm_kf0[KV8 ? BN : 1];   // per-key score factors
+  __shared__ __attribute__((aligned(16))) float sm_kf1[KV8 ? BN : 1];
+  __shared__ __attribute__((aligned(1024))) int8_t sm_stage0[KV8 ? 2 * QT::STAGE : 16];   // K, V codes
+  __shared__ __attribute__((aligned(1024))) int8_t sm_stage1[KV8 ? 2 * QT::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) float sm_sst0[KV8 ? QT::SCALES : 1];            // their scales
+  __shared__ __attribute__((aligned(16))) float sm_sst1[KV8 ? QT::SCALES : 1];
   __shared__ int sm_last;
   constexpr int ROWS = NW * 32 * NQB;   // query rows per block
 
@@ -760,79 +807,121 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
     const uint16_t* vc = p.Vc + int64_t(h) * D;
     A.load_q(p.Q, q0, p.nq, rs, h, p.c);
 
-    // Loads of tile j into buffer PB.  int8 tiles go to the staging area first and are
-    // widened by finish().  Returns true when a widening is pending.
-    auto issue = [&](auto pb, int j) __attribute__((always_inline)) -> bool {
-      constexpr int PB = decltype(pb)::value;
+    // Tile j is computed from K/V buffer j & 1.  A bf16 tile is copied there one step
+    // ahead (while tile j - 1 is computed).  A quantised cache tile goes two steps
+    // ahead: its codes and scales are copied to staging area j & 1 while tile j - 2 is
+    // computed, and each wave widens the rows it copied while the score MFMAs of tile
+    // j - 1 run, so the conversions overlap them instead of delaying the barrier.
+    // quantised tiles: the partial cache tiles and every tile from the full cache tiles on
+    auto quant = [&](int j) __attribute__((always_inline)) -> bool {
+      if (!KV8 || j >= jend) return false;
+      return j >= order.own_end() || (j < order.npart() && order.at(j).seg == 0);
+    };
+    auto issue_bf16 = [&](auto pb, auto full, int j) __attribute__((always_inline)) {
+      const int PB = pb;
+      uint16_t* lk = PB ? sm_k1 : sm_k0;
+      uint16_t* lv = PB ? sm_v1 : sm_v0;
       const TileInfo t = order.at(j);
-      if (KV8 && t.seg == 0) {
-        QTile<D, NW, KVQ>::issue(p, h, t, sm_stage, PB ? sm_ks1 : sm_ks0, PB ? sm_vs1 : sm_vs0, wave, lane);
-        return true;
+      const uint16_t* gk = t.seg == 0 ? ck : kc;
+      const uint16_t* gv = t.seg == 0 ? cv : vc;
+      if (decltype(full)::value) {
+        const int64_t base = int64_t(t.start) * rs;
+        dma_full<D, NW>(gk + base, gv + base, loff, lk, lv, wave);
+      } else {
+        dma_tile<D, NW>(gk, gv, rs, t, lk, lv, wave, lane);
       }
-      dma_tile<D, NW>(t.seg == 0 ? ck : kc, t.seg == 0 ? cv : vc, rs, t, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0,
-                      wave, lane);
-      return false;
     };
-    // A full bf16 tile (every tile after the partial ones, except int8 cache tiles).
-    auto issue_full = [&](auto pb, int j) __attribute__((always_inline)) {
-      constexpr int PB = decltype(pb)::value;
-      const TileInfo t = order.at(j);
-      const int64_t base = int64_t(t.start) * rs;
-      dma_full<D, NW>((t.seg == 0 ? ck : kc) + base, (t.seg == 0 ? cv : vc) + base, loff, PB ? sm_k1 : sm_k0,
-                      PB ? sm_v1 : sm_v0, wave);
+    auto issue_codes = [&](auto pb, int j) __attribute__((always_inline)) {
+      const int PB = pb;
+      QT::issue(p, h, order.at(j), PB ? sm_stage1 : sm_stage0, PB ? sm_sst1 : sm_sst0, wave, lane);
     };
-    auto finish = [&](auto pb, bool pending) __attribute__((always_inline)) {
-      constexpr int PB = decltype(pb)::value;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (KV8 && pending) QTile<D, NW, KVQ>::widen(sm_stage, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, wave, lane);
-      __syncthreads();
+    auto widen = [&](auto pb) __attribute__((always_inline)) {
+      const int PB = pb;
+      QT::widen(PB ? sm_stage1 : sm_stage0, PB ? sm_sst1 : sm_sst0, PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0,
+                PB ? sm_kf1 : sm_kf0, p.c, wave, lane);
+    };
+    // wait for everything but (keep = true) the codes of the tile two steps ahead
+    auto wait_vm = [](bool keep) __attribute__((always_inline)) {
+      if (KV8 && keep) vm_wait<QT::OPS>();
+      else vm_wait<0>();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // Full tiles: prefetch the next tile into the other buffer, compute this one.  The
-    // buffer parity is a template argument so LDS accesses name a fixed buffer.
-    // KIND 1: int8 cache tiles (scaled), 2: bf16 tiles (cache or own chunk).
-    auto step = [&](auto pb, auto kind, int j) __attribute__((always_inline)) {
-      constexpr int PB = decltype(pb)::value;
-      constexpr int KIND = decltype(kind)::value;
-      bool pend = false;
-      if (j + 1 < jend) {
-        if (KIND == 2 || !KV8) {
-          issue_full(std::integral_constant<int, PB ^ 1>{}, j + 1);
-        } else {
-          pend = issue(std::integral_constant<int, PB ^ 1>{}, j + 1);
+    using Full = std::true_type;
+    using Part = std::false_type;
+    // One step: compute tile j (buffer pb = j & 1), ready tile j + 1 and copy the codes
+    // of tile j + 2.  MODE 0: a partial tile (masked path, everything decided at run
+    // time); MODE 2: a full bf16 tile (followed by bf16 tiles or, in a quantised cache,
+    // by the full cache tiles); MODE 1: a full quantised cache tile, followed by
+    // quantised tiles only.  Copies straight into a tile buffer never occur in MODE 1,
+    // so the compiler has no reason to wait for them before the widened rows are stored.
+    auto step = [&](auto pb, auto mode, int j) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode)::value;
+      const int PB = pb;
+      // (MODE 2: tile j is past the partial tiles, so a later tile is quantised exactly
+      // when it lies in the full cache tiles)
+      const bool q1 = MODE == 1 ? j + 1 < jend
+                    : MODE == 2 ? KV8 && j + 1 < jend && j + 1 >= order.own_end() : quant(j + 1);
+      const bool q2 = MODE == 1 ? j + 2 < jend
+                    : MODE == 2 ? KV8 && j + 2 < jend && j + 2 >= order.own_end() : quant(j + 2);
+      const bool b1 = MODE != 1 && j + 1 < jend && !q1;
+      if (b1) {
+        if (MODE == 0 && j + 1 < order.npart()) issue_bf16(PB ^ 1, Part{}, j + 1);
+        else issue_bf16(PB ^ 1, Full{}, j + 1);
+      }
+      if (q2) issue_codes(pb, j + 2);
+      auto mid = [&]() __attribute__((always_inline)) {
+        if (q1) {
+          wait_vm(q2);
+          widen(PB ^ 1);
         }
+      };
+      constexpr bool MASK = MODE == 0;
+      constexpr bool SC = MODE == 1 || (MODE == 0 && KV8);
+      int cnt = BN;
+      bool scaled = SC;
+      if constexpr (MODE == 0) {
+        const TileInfo t = order.at(j);
+        cnt = t.cnt;
+        scaled = KV8 && t.seg == 0;
       }
-      A.template tile<false, KIND == 1>(PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_ks1 : sm_ks0,
-                                        PB ? sm_vs1 : sm_vs0, BN);
-      finish(std::integral_constant<int, PB ^ 1>{}, pend);
+      A.template tile<MASK, SC>(PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_kf1 : sm_kf0, cnt, scaled, mid);
+      // everything this wave copied (the next tile, the codes two tiles ahead) has
+      // landed before the barrier (an unconditional wait: measured faster than one
+      // only after a tile copy)
+      vm_wait<0>();
+      __syncthreads();
     };
-    auto run = [&](auto kind, int j, int end) __attribute__((always_inline)) -> int {
-      if (j < end && (j & 1)) step(I1{}, kind, j++);
+    auto run = [&](auto mode, int j, int end) __attribute__((always_inline)) -> int {
+      if (j < end && (j & 1)) step(I1{}, mode, j++);
       for (; j + 1 < end; j += 2) {
-        step(I0{}, kind, j);
-        step(I1{}, kind, j + 1);
+        step(I0{}, mode, j);
+        step(I1{}, mode, j + 1);
       }
-      if (j < end) step(I0{}, kind, j++);
+      if (j < end) step(I0{}, mode, j++);
       return j;
     };
+    using M0 = std::integral_constant<int, 0>;
+    using M1 = std::integral_constant<int, 1>;
+    using M2 = std::integral_constant<int, 2>;
 
-    if (ja & 1) finish(I1{}, issue(I1{}, ja));
-    else finish(I0{}, issue(I0{}, ja));
-    int j = ja;
-    // Partial tiles (at most two): one generic masked path with run-time buffer choice.
-    for (; j < min(jb, order.npart()); ++j) {
-      bool pend = false;
-      if (j + 1 < jb) pend = (j & 1) ? issue(I0{}, j + 1) : issue(I1{}, j + 1);
-      const TileInfo t = order.at(j);
-      const bool odd = j & 1;
-      A.template tile<true, KV8>(odd ? sm_k1 : sm_k0, odd ? sm_v1 : sm_v0, odd ? sm_ks1 : sm_ks0,
-                                 odd ? sm_vs1 : sm_vs0, t.cnt, KV8 && t.seg == 0);
-      if (j & 1) finish(I0{}, pend);
-      else finish(I1{}, pend);
+    {  // tile ja into its buffer (and the codes of tile ja + 1 under way)
+      const bool q0 = quant(ja), q1 = quant(ja + 1);
+      const int P0 = ja & 1;
+      if (q0) issue_codes(P0, ja);
+      else if (ja < order.npart()) issue_bf16(P0, Part{}, ja);
+      else issue_bf16(P0, Full{}, ja);
+      if (q1) issue_codes(P0 ^ 1, ja + 1);
+      wait_vm(q1);
+      if (q0) widen(P0);
+      __syncthreads();
     }
-    if (KV8) j = run(std::integral_constant<int, 1>{}, j, min(jb, order.full1_end()));
-    run(std::integral_constant<int, 2>{}, j, jb);
+    // order: partial tiles (one per run of keys at most), full own-chunk tiles, full
+    // cache tiles
+    int j = ja;
+    for (; j < min(jb, order.npart()); ++j) step(j & 1, M0{}, j);
+    if (KV8) j = run(M2{}, j, min(jb, order.own_end()));
+    run(std::integral_constant<int, KV8 ? 1 : 2>{}, j, jb);
 
     if (npc == 1) {
       A.store(p.out, q0, p.nq, rs, h);

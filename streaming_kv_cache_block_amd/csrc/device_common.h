@@ -96,6 +96,24 @@ __device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t w, int byte0) {
   else return i8x2_to_bf16x2(w, byte0);
 }
 
+// Two codes (bytes byte0, byte0 + 1 of w) times the scale s, each product rounded
+// once to fp32 and then to bf16 (nearest even): the dequantised value as bf16.
+template <int FMT>
+__device__ __forceinline__ uint32_t dequant2_bf16x2(uint32_t w, int byte0, float s) {
+  float f0, f1;
+  if constexpr (FMT == kKvFp8) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = byte0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    f0 = v[0];
+    f1 = v[1];
+  } else {
+    f0 = (float)(int8_t)((w >> (8 * byte0)) & 0xffu);
+    f1 = (float)(int8_t)((w >> (8 * (byte0 + 1))) & 0xffu);
+  }
+  return pack_bf16x2(f0 * s, f1 * s);
+}
+
 // Two fp32 values (|y| <= 448) -> two OCP E4M3 codes, round to nearest even, into the
 // low (hi_half = false) or high 16 bits of `old`.
 __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float y0, float y1, uint32_t old, bool hi_half) {

@@ -21,7 +21,8 @@
 #include <cstdint>
 
 #ifdef __HIPCC__
-#define LL_HD __host__ __device__
+// always inlined: in the attention kernel the piece body is inlined into for_each_piece
+#define LL_HD __host__ __device__ __attribute__((always_inline))
 #else
 #define LL_HD
 #endif

@@ -86,20 +86,22 @@ def compare_attention(gpu_out, ref, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS, sc
     return mx, mn
 
 
-def compare_rounding_bound(gpu_out, ref, ref_absv, what):
+def compare_rounding_bound(gpu_out, ref, ref_absv, what, kv="bf16"):
     """Elementwise bound derived from the kernel's roundings, for inputs where outputs
     are large (peaked or wide-spread scores), where the contract's absolute bounds
-    say little.  The kernel rounds each probability (times the V scale of a low-bit
-    tile) to bf16 before the P*V product and normalises by the sum of what it applied
-    or by the fp32 sum: each applied weight is off by at most 2^-8 relative, twice,
-    so |sum_j (w~_j - w_j) v_j| <= 2^-7 sum_j p_j |v_j|; the output's bf16 rounding adds
-    at most 2^-8 |out|.  ref_absv is sum_j p_j |v_j| (the oracle run with |V|)."""
+    say little.  The kernel rounds each probability to bf16 before the P*V product and
+    normalises by the sum of what it applied: each applied weight is off by at most
+    2^-8 relative, twice, so |sum_j (w~_j - w_j) v_j| <= 2^-7 sum_j p_j |v_j|.  A low-bit
+    cache's values enter P*V dequantised and rounded to bf16 (2^-8 relative), which
+    adds 2^-8 sum_j p_j |v_j|.  The output's bf16 rounding adds at most 2^-8 |out|.
+    ref_absv is sum_j p_j |v_j| (the oracle run with |V|)."""
     got = bf16.to_f32(gpu_out if isinstance(gpu_out, np.ndarray) else synth.to_bits(gpu_out)).astype(np.float64)
     ref = ref.astype(np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got - ref)
-    bound = 2.0 ** -7 * ref_absv.astype(np.float64) + 2.0 ** -8 * np.abs(ref) + 1e-6
+    coef = 2.0 ** -7 + (2.0 ** -8 if kv in ("int8", "fp8") else 0.0)
+    bound = coef * ref_absv.astype(np.float64) + 2.0 ** -8 * np.abs(ref) + 1e-6
     worst = np.unravel_index(int(np.argmax(err - bound)), err.shape)
     assert (err <= bound).all(), (f"{what}: err {err[worst]:.3g} > bound {bound[worst]:.3g} at {worst} "
                                   f"(ref {ref[worst]:.3g}); {int((err > bound).sum())} outside")

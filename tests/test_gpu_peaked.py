@@ -89,7 +89,7 @@ def _check_all_rows(torch, cache, hist, kv, W, q, kc, vc, what, scale_gate):
     t0 = time.time()
     ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv=kv)
     ref_abs = attention.chunk_attention(q, kc, abs_bits(vc), AbsHistory(hist), hist.f0, S, W, T, kv=kv)
-    mx, worst = compare_rounding_bound(out, ref, ref_abs, what)
+    mx, worst = compare_rounding_bound(out, ref, ref_abs, what, kv=kv)
     msg = f"{what}: max-abs {mx:.3g}, worst err/bound {worst:.3f}, max|ref| {np.abs(ref).max():.3g}"
     if scale_gate:
         mx, mn = compare_attention(out, ref, what, scale_gate=True)

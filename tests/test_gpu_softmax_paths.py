@@ -91,6 +91,6 @@ def test_wide_score_spread(torch_gpu, D, kv):
         out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
         ref = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv=kv)
         ref_abs = attention.chunk_attention(q, kc, abs_bits(vc), AbsHistory(hist), f0, S, W, T, kv=kv)
-        compare_rounding_bound(out, ref, ref_abs, f"spread D={D} kv={kv} chunk {chunk}")
+        compare_rounding_bound(out, ref, ref_abs, f"spread D={D} kv={kv} chunk {chunk}", kv=kv)
         cache.append(0, synth.to_device(kc), synth.to_device(vc))
         hist.append(kc, vc)
