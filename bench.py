@@ -17,7 +17,7 @@ as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--no-components] [--no-rollouts]
-                    [--workload steady|rollout|long_int8|recache|sweep|append]
+                    [--workload steady|rollout|long_int8|recache|sweep|append|steady_int8|steady_fp8]
 """
 
 import argparse

@@ -28,7 +28,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;      // 16-byte vectors in flight per thread (copies)
-constexpr int kQuantRows = 2;   // rows per lane group of the quantising writes
+constexpr int kQuantRows = 2;     // rows per lane group of the quantising writes
+constexpr int kQuantValues = 16;  // values of a row per lane in the quantising writes
 
 // grid: x = block within the frame, y = plan entry, z = 0 (K) / 1 (V)
 __global__ __launch_bounds__(kThreads) void copy_frames_kernel(const WriteParams p, int64_t vecs_per_frame) {
@@ -73,7 +74,7 @@ __device__ __forceinline__ float div_by_M(float a) {
   return __builtin_fmaf(r, yM, q0);
 }
 
-// Max over the LPR (8 or 16) lanes of a row, every lane ends with it: DPP inside quads
+// Max over the LPR (4, 8 or 16) lanes of a row, every lane ends with it: DPP inside quads
 // (xor 1, xor 2), then the half-row (8 lanes) and row (16 lanes) mirrors.
 template <int LPR>
 __device__ __forceinline__ float row_max(float v) {
@@ -85,16 +86,17 @@ __device__ __forceinline__ float row_max(float v) {
       default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
     }
   };
-  static_assert(LPR == 8 || LPR == 16, "rows of 8 or 16 lanes");
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "rows of 4, 8 or 16 lanes");
   v = fmaxf(v, dpp(v, 0xB1));
   v = fmaxf(v, dpp(v, 0x4E));
-  v = fmaxf(v, dpp(v, 0x141));
+  if constexpr (LPR >= 8) v = fmaxf(v, dpp(v, 0x141));
   if constexpr (LPR == 16) v = fmaxf(v, dpp(v, 0x140));
   return v;
 }
 
-// One (token, head) row of D values per LPR = D / 8 lanes (aligned to DPP rows); each
-// lane owns 8 values of RPG rows, whose loads are all issued before any arithmetic.
+// One (token, head) row of D values per LPR = D / 16 lanes (aligned to DPP rows); each
+// lane owns 16 consecutive values of RPG rows (two 16-byte loads each, all issued before
+// any arithmetic) and stores their 16 codes with one 16-byte store.
 //
 // Division: q = rint(n / a) with n = x * M needs the correctly rounded quotient.  With
 // y = RN(1/a) and q0 = RN(n * y) within one ulp of n/a, the residual r = n - a * q0 is
@@ -109,7 +111,8 @@ __device__ __forceinline__ float row_max(float v) {
 template <int D, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParams p) {
   constexpr float M = FMT == kKvFp8 ? 448.0f : 127.0f;
-  constexpr int LPR = D / 8;
+  constexpr int VPL = kQuantValues;
+  constexpr int LPR = D / VPL;
   constexpr int GROUPS = kThreads / LPR;
   constexpr int RPG = kQuantRows;
   const int e = blockIdx.y;
@@ -120,36 +123,40 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
   int8_t* dst = static_cast<int8_t*>(isv ? p.dstV : p.dstK) + int64_t(p.plan_slot[e]) * p.rows_per_frame * D;
   float* dsc = (isv ? p.dstVs : p.dstKs) + int64_t(p.plan_slot[e]) * p.rows_per_frame;
 
-  u32x4 w[RPG];
+  u32x4 w[RPG][VPL / 8];
 #pragma unroll
   for (int rr = 0; rr < RPG; ++rr) {
     const int64_t row = row0 + rr;
-    w[rr] = row < p.rows_per_frame ? *reinterpret_cast<const u32x4*>(src + row * D + 8 * sub)
-                                   : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < VPL / 8; ++h)
+      w[rr][h] = row < p.rows_per_frame ? *reinterpret_cast<const u32x4*>(src + row * D + VPL * sub + 8 * h)
+                                        : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int rr = 0; rr < RPG; ++rr) {
     const int64_t row = row0 + rr;
-    float x[8];
+    float x[VPL];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __builtin_bit_cast(float, w[rr][k] << 16);
-      x[2 * k + 1] = __builtin_bit_cast(float, w[rr][k] & 0xffff0000u);
-    }
+    for (int h = 0; h < VPL / 8; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * h + 2 * k] = __builtin_bit_cast(float, w[rr][h][k] << 16);
+        x[8 * h + 2 * k + 1] = __builtin_bit_cast(float, w[rr][h][k] & 0xffff0000u);
+      }
     float a = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
+    for (int k = 0; k < VPL; ++k) a = fmaxf(a, fabsf(x[k]));
     a = row_max<LPR>(a);
 
     float scale = 0.0f;
-    uint32_t packed[2] = {0u, 0u};
+    uint32_t packed[VPL / 4] = {};
     if (a > 0.0f) {
       const bool plain = a < 0x1p-100f || a > 0x1p+120f;
       scale = plain ? a / M : div_by_M<FMT>(a);
       const float y = plain ? 1.0f / a : rcp_rn_bf16(a);
-      float qq[8];
+      float qq[VPL];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < VPL; ++k) {
         const float n = x[k] * M;   // exact for bf16 x unless it overflows
         if (plain) {
           qq[k] = fminf(fmaxf(n / a, -M), M);
@@ -160,29 +167,29 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
         }
       }
       if constexpr (FMT == kKvFp8) {
-        // The FMA correction turns a -0 quotient into +0; the IEEE quotient has the sign
-        // of x (a > 0), and E4M3 keeps the sign of zero.
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qq[k] = __builtin_copysignf(qq[k], x[k]);
+        for (int k = 0; k < VPL; ++k) qq[k] = __builtin_copysignf(qq[k], x[k]);
 #pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
+        for (int w2 = 0; w2 < VPL / 4; ++w2) {
           packed[w2] = f32x2_to_e4m3x2(qq[4 * w2], qq[4 * w2 + 1], 0u, false);
           packed[w2] = f32x2_to_e4m3x2(qq[4 * w2 + 2], qq[4 * w2 + 3], packed[w2], true);
         }
       } else {
-        uint32_t t[8];
+        uint32_t t[VPL];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) t[k] = __builtin_bit_cast(uint32_t, qq[k] + 12582912.0f);
-        // low bytes of t[4j .. 4j+3] -> bytes 0..3 of one word
+        for (int k = 0; k < VPL; ++k) t[k] = __builtin_bit_cast(uint32_t, qq[k] + 12582912.0f);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < VPL / 4; ++j)
           packed[j] = __builtin_amdgcn_perm(t[4 * j + 1], t[4 * j], 0x0c0c0400u) |
                       __builtin_amdgcn_perm(t[4 * j + 3], t[4 * j + 2], 0x04000c0cu);
       }
     }
     if (row < p.rows_per_frame) {
-      __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, reinterpret_cast<u32x2*>(dst + row * D + 8 * sub));
-      if (sub == 0) dsc[row] = scale;   // 4-byte scales of adjacent rows merge in the L2
+#pragma unroll
+      for (int h = 0; h < VPL / 16; ++h)
+        __builtin_nontemporal_store(u32x4{packed[4 * h], packed[4 * h + 1], packed[4 * h + 2], packed[4 * h + 3]},
+                                    reinterpret_cast<u32x4*>(dst + row * D + VPL * sub + 16 * h));
+      if (sub == 0) dsc[row] = scale;
     }
   }
 }
@@ -198,7 +205,7 @@ hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t 
     hipLaunchKernelGGL(copy_frames_kernel, grid, dim3(kThreads), 0, s, p, vecs);
     return hipGetLastError();
   }
-  const int rows_per_block = kThreads / (D / 8) * kQuantRows;
+  const int rows_per_block = kThreads / (D / kQuantValues) * kQuantRows;
   dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
   if (D == 128 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<128, kKvInt8>), grid, dim3(kThreads), 0, s, p);
   else if (D == 64 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<64, kKvInt8>), grid, dim3(kThreads), 0, s, p);
