@@ -65,6 +65,10 @@ def test_create_rejects_invalid_arguments_before_touching_hip(L):
         assert L.ll_last_error()
         assert h.value is None
     assert L.ll_cache_create(1, 2, 64, 16, 3, 6, 0, None) == ll.LL_ERR_INVALID
+    # shot sinks: S + Ss + W above the slot limit, a negative shot sink
+    for args in [(1, 12, 128, 1560, 3, 3, 123, 0), (1, 12, 128, 1560, 3, -1, 12, 0)]:
+        assert L.ll_cache_create_shots(*args, ctypes.byref(h)) == ll.LL_ERR_INVALID, args
+        assert h.value is None
 
 
 def test_calls_on_null_handle_are_invalid(L):

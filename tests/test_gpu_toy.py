@@ -252,3 +252,27 @@ def test_quantisation_edge_rows_bit_exact(torch_gpu, kv):
         cache.append(0, synth.to_device(kb), synth.to_device(vb))
         hist.append(kb, vb)
         check_slots(cache, 0, hist, kv=kv)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_maximum_slot_count(torch_gpu, kv):
+    """S + W = 128 slots (the largest cache the library accepts): sink 8, window 120,
+    16 tokens per frame, 2 heads x 128.  50 chunks of 3 frames wrap the 120-slot ring
+    once (f0 = 150); the attention of the chunks that see the most keys (128 cached frames
+    plus the own chunk: 2096 keys, 33 key tiles) is compared with the oracle in full, and
+    the slot contents bit for bit at the end."""
+    T, H, D, S, W, C = 16, 2, 128, 8, 120, 3
+    assert S + W == ll.MAX_SLOTS
+    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
+    hist = History(S, W, T)
+    shape = (C * T, H, D)
+    for k in range(50):
+        q, kc, vc = (synth.normal_bf16(shape, 1.0, 780, t, k) for t in range(3))
+        if hist.f0 >= S + W or k in (0, 1, 2):
+            out = cache.attn(0, synth.to_device(q), synth.to_device(kc), synth.to_device(vc))
+            ref = attention.chunk_attention(q, kc, vc, hist, hist.f0, S, W, T, kv=kv)
+            compare_attention(out, ref, f"max slots kv={kv} chunk {k} f0={hist.f0}")
+        cache.append(0, synth.to_device(kc), synth.to_device(vc))
+        hist.append(kc, vc)
+    assert hist.f0 == 150
+    check_slots(cache, 0, hist, kv=kv)
