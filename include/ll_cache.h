@@ -37,8 +37,8 @@
  * Debug build (libllcache_debug.so: same kernels and interface, host side compiled
  * with LL_DEBUG), for finding slot bookkeeping mistakes:
  *   - every slot of a new cache is filled with NaN (bf16 caches: NaN values;
- *     int8 / fp8 caches: NaN per-row scales), and a recache or window-only recache
- *     fills the slots it rewrites with NaN before writing them, so a slot read
+ *     int8 / fp8 caches: NaN per-row scales), and a recache, window-only recache or
+ *     fused recache fills the slots it rewrites with NaN before writing them, so a slot read
  *     before a frame reached it turns the output into NaN;
  *   - an attention call whose visible slots include one that holds no frame fails
  *     with LL_ERR_STATE before launching anything;

@@ -568,6 +568,9 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
     if (first < 0) first = e.slot;
     else p.plan_slot2[size_t(e.src)] = e.slot;
   }
+#ifdef LL_DEBUG
+  LL_TRY(poison_planned(c, layer, plan, static_cast<hipStream_t>(stream)));
+#endif
   hipError_t e = ll::launch_kv_project_to_cache(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "recache_from_hidden launch");
   return ok();

@@ -4,9 +4,10 @@ Every slot of a fresh debug cache is poisoned (bf16 NaN, or NaN scales for int8 
 and the slots a recache rewrites are poisoned again just before.  So:
   * a toy rollout through the debug library gives finite outputs, byte for byte the
     normal library's: attention never read a slot no frame was written to;
-  * after a recache, and after a window-only recache, no retained slot holds poison: the
-    rewrite reached every slot it owns (and the window-only recache left the sink as it
-    was, not poisoned).
+  * after a recache, a window-only recache and a fused projection into the slots, no
+    retained slot holds poison: the rewrite reached every slot it owns (the window-only
+    recache left the sink as it was, not poisoned), and the fused rewrite's bytes are
+    the normal library's.
 """
 
 import numpy as np
@@ -81,5 +82,18 @@ def test_debug_library_poisons_and_matches(torch_gpu, kv):
     hist.recache_window(K_w, V_w)
     assert not _poisoned(dbg.slot_bytes(0), kv).any()
     check_slots(dbg, 0, hist, kv=kv)
+    # fused projection into the slots: poisoned first, then every retained slot written,
+    # byte for byte what the normal library writes
+    d_in = 128
+    n = len(hist.model.retained_frames())
+    h = synth.to_device(synth.normal_bf16((n * T, d_in), 1.0, 773, 0))
+    w_k = synth.to_device(synth.normal_bf16((H * D, d_in), 0.05, 773, 1))
+    w_v = synth.to_device(synth.normal_bf16((H * D, d_in), 0.05, 773, 2))
+    dbg.recache_from_hidden(0, h, w_k, w_v)
+    ref.recache_from_hidden(0, h, w_k, w_v)
+    got, want = dbg.slot_bytes(0), ref.slot_bytes(0)
+    assert not _poisoned(got, kv).any()
+    for name in got:
+        assert np.array_equal(got[name].view(np.uint8), want[name].view(np.uint8)), name
     dbg.close()
     ref.close()
