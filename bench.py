@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sink+window attention TFLOP/s & latent frames/s per layer; % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+CEILING_LIB = os.path.join(ROOT, "streaming_kv_cache_block_amd", "libllceiling.so")
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 POOL = 8                       # distinct input sets cycled through the passes
 
@@ -144,6 +145,51 @@ class ClockSampler:
         return {"median_mhz": float(np.median(a)), "min_mhz": float(a.min()), "max_mhz": float(a.max()),
                 "samples": int(a.size), "source": "amdsmi gpu metrics: mean of the 8 XCDs' current GFX clocks, "
                                                   "samples at >= 90% GFX activity"}
+
+
+def mfma_ceiling(torch, seconds=1.0):
+    """The measured bf16 MFMA ceiling (libllceiling.so): every wave of 8 per CU (two per
+    SIMD, as in the attention kernel) issues independent 32x32x16 bf16 MFMAs and nothing
+    else.  Launches run back to back for about `seconds`, each timed with events on the
+    launch stream; the figure is the median over the second half, once the clock has
+    settled under the load (short bursts run faster than sustained work), with the shader
+    clock sampled over the same launches."""
+    import ctypes
+    L = ctypes.CDLL(CEILING_LIB)
+    L.llc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * n_cu, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = L.llc_mfma_loop(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"MFMA ceiling launch failed ({rc})")
+
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    n = 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n = max(20, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    with ClockSampler() as clk:
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in ev[n // 2:]]
+    ms = _stats(times)["median"]
+    flop = float(blocks) * 4 * iters * 4 * 32768
+    return {"tflops": flop / ms / 1e9, "frac_of_nominal": flop / ms / 1e9 / PEAK_BF16_TFLOPS, "ms": ms,
+            "launches": n, "sclk": clk.summary(),
+            "what": "independent 32x32x16 bf16 MFMAs only, 8 waves per CU, sustained (second half of ~1 s)"}
 
 
 def run_steady(torch, ll, synth, cfg, steps, warmup, kv="bf16"):
@@ -682,6 +728,7 @@ def main():
     r = run_steady(torch, ll, synth, cfg, args.steps, args.warmup)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     value = cfg.chunk_frames * args.steps / r["wall_s"]
+    ceiling = mfma_ceiling(torch)
 
     components = {}
     if not args.no_components:
@@ -737,7 +784,8 @@ def main():
                      "traffic": _traffic_from_profiles(),
                      "kernel": "attn_kernel (sink+window attention, one pass)",
                      "flop_per_launch": r["attn_flops"], "avg_launch_ms": r["attn_ms"],
-                     "median_launch_ms": r["attn_ms_stats"]["median"], "sclk": r["sclk"]},
+                     "median_launch_ms": r["attn_ms_stats"]["median"], "sclk": r["sclk"],
+                     "ceiling": ceiling, "frac_of_ceiling": r["attn_tflops"] / ceiling["tflops"]},
         "attn_tflops": r["attn_tflops"],
         "components": components,
     }

@@ -4,7 +4,8 @@
 
 Compiles every HIP source with hipcc for gfx950 into objects under ``_build/`` and
 links ``streaming_kv_cache_block_amd/libllcache.so``; also builds the seeded input
-generator's device twin ``synth/libsynthfill.so`` (input preparation, not the product).  Packed-FP32 instruction
+generator's device twin ``synth/libsynthfill.so`` (input preparation, not the product)
+and ``libllceiling.so`` (the measured MFMA ceiling bench.py reports beside the roofline).  Packed-FP32 instruction
 selection is switched off for device code.  ``slots_cli`` is built with g++ and
 the host sanitizers (it has no device code).
 """
@@ -27,6 +28,9 @@ SLOTS_CLI = os.path.join(BUILD, "slots_cli")
 
 HIP_SOURCES = ["attn.hip", "kvwrite.hip", "gemm.hip", "cache.cpp"]
 ARCH = "gfx950"
+# measured MFMA ceiling for the roofline (bench.py): a library of its own, not the product
+CEILING_SRC = os.path.join(CSRC, "ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libllceiling.so")
 # seeded input generator's device twin (synth/): a library of its own, not the product
 SYNTH_SRC = os.path.join(ROOT, "synth", "csrc", "fill.hip")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libsynthfill.so")
@@ -73,6 +77,11 @@ def build(verbose: bool = False) -> str:
         _run([hipcc, "-x", "hip", *HIP_FLAGS, "-shared", SYNTH_SRC, "-o", tmp])
         os.replace(tmp, SYNTH_LIB)
 
+    def ceiling_lib():
+        tmp = CEILING_LIB + ".tmp"
+        _run([hipcc, "-x", "hip", *HIP_FLAGS, "-shared", CEILING_SRC, "-o", tmp])
+        os.replace(tmp, CEILING_LIB)
+
     def compile_debug_host():
         obj = os.path.join(BUILD, "cache_debug.o")
         _run([hipcc, "-x", "hip", *HIP_FLAGS, "-DLL_DEBUG", "-c", os.path.join(CSRC, "cache.cpp"), "-o", obj])
@@ -80,9 +89,11 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(6, len(HIP_SOURCES) + 2)) as ex:
         synth_job = ex.submit(synth_lib)
+        ceiling_job = ex.submit(ceiling_lib)
         debug_job = ex.submit(compile_debug_host)
         objs = list(ex.map(compile_one, HIP_SOURCES))
         synth_job.result()
+        ceiling_job.result()
         debug_obj = debug_job.result()
     for target, host in ((LIB, objs[-1]), (LIB_DEBUG, debug_obj)):
         tmp = target + ".tmp"

@@ -90,3 +90,18 @@ def test_clock_sampler_reports_rather_than_raises():
         pass
     s = clk.summary()
     assert ("median_mhz" in s) or ("error" in s)
+
+
+def test_mfma_ceiling_library_exports_its_loop_and_checks_arguments():
+    """libllceiling.so (the measured MFMA ceiling beside the roofline) is built with the
+    package and rejects bad arguments before any HIP call (so this runs on the CPU)."""
+    import ctypes
+    import os
+    import bench
+    assert os.path.exists(bench.CEILING_LIB), bench.CEILING_LIB
+    L = ctypes.CDLL(bench.CEILING_LIB)
+    L.llc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    buf = ctypes.create_string_buffer(16)
+    assert L.llc_mfma_loop(None, 1, 1, None) != 0
+    assert L.llc_mfma_loop(ctypes.addressof(buf), 0, 1, None) != 0
+    assert L.llc_mfma_loop(ctypes.addressof(buf), 1, 0, None) != 0
