@@ -147,23 +147,32 @@ class ClockSampler:
                                                   "samples at >= 90% GFX activity"}
 
 
-def mfma_ceiling(torch, seconds=1.0):
+def mfma_ceiling(torch, synth=None, seconds=1.0):
     """The measured bf16 MFMA ceiling (libllceiling.so): every wave of 8 per CU (two per
     SIMD, as in the attention kernel) issues independent 32x32x16 bf16 MFMAs and nothing
     else.  Launches run back to back for about `seconds`, each timed with events on the
     launch stream; the figure is the median over the second half, once the clock has
     settled under the load (short bursts run faster than sustained work), with the shader
-    clock sampled over the same launches."""
+    clock sampled over the same launches.  With `synth`, the operands are seeded N(0, 1)
+    bf16 draws, a different fragment pair in each MFMA (the matrix cores draw more power
+    on such bits, so the device holds a lower clock); without, one pair of operands with
+    few mantissa bits set (a best case)."""
     import ctypes
     L = ctypes.CDLL(CEILING_LIB)
     L.llc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.llc_mfma_loop_data.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     blocks, iters = 2 * n_cu, 4096
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    data = synth.normal_bf16_device((256 * 64,), 1.0, 977, 1) if synth is not None else None
     stream = torch.cuda.current_stream()
 
     def launch():
-        rc = L.llc_mfma_loop(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        if data is None:
+            rc = L.llc_mfma_loop(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        else:
+            rc = L.llc_mfma_loop_data(out.data_ptr(), data.data_ptr(), blocks, iters, stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"MFMA ceiling launch failed ({rc})")
 
@@ -187,9 +196,12 @@ def mfma_ceiling(torch, seconds=1.0):
     times = [a.elapsed_time(b) for a, b in ev[n // 2:]]
     ms = _stats(times)["median"]
     flop = float(blocks) * 4 * iters * 4 * 32768
+    what = ("seeded N(0,1) bf16 operands, a new fragment pair per MFMA" if data is not None
+            else "one operand pair with few mantissa bits set")
     return {"tflops": flop / ms / 1e9, "frac_of_nominal": flop / ms / 1e9 / PEAK_BF16_TFLOPS, "ms": ms,
             "launches": n, "sclk": clk.summary(),
-            "what": "independent 32x32x16 bf16 MFMAs only, 8 waves per CU, sustained (second half of ~1 s)"}
+            "what": "independent 32x32x16 bf16 MFMAs only, 8 waves per CU, sustained (second half of ~1 s); "
+                    + what}
 
 
 def run_steady(torch, ll, synth, cfg, steps, warmup, kv="bf16"):
@@ -728,7 +740,8 @@ def main():
     r = run_steady(torch, ll, synth, cfg, args.steps, args.warmup)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     value = cfg.chunk_frames * args.steps / r["wall_s"]
-    ceiling = mfma_ceiling(torch)
+    ceiling = mfma_ceiling(torch, synth)
+    ceiling_low_bits = mfma_ceiling(torch)
 
     components = {}
     if not args.no_components:
@@ -785,7 +798,8 @@ def main():
                      "kernel": "attn_kernel (sink+window attention, one pass)",
                      "flop_per_launch": r["attn_flops"], "avg_launch_ms": r["attn_ms"],
                      "median_launch_ms": r["attn_ms_stats"]["median"], "sclk": r["sclk"],
-                     "ceiling": ceiling, "frac_of_ceiling": r["attn_tflops"] / ceiling["tflops"]},
+                     "ceiling": ceiling, "frac_of_ceiling": r["attn_tflops"] / ceiling["tflops"],
+                     "ceiling_low_bits": ceiling_low_bits},
         "attn_tflops": r["attn_tflops"],
         "components": components,
     }

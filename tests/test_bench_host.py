@@ -105,3 +105,10 @@ def test_mfma_ceiling_library_exports_its_loop_and_checks_arguments():
     assert L.llc_mfma_loop(None, 1, 1, None) != 0
     assert L.llc_mfma_loop(ctypes.addressof(buf), 0, 1, None) != 0
     assert L.llc_mfma_loop(ctypes.addressof(buf), 1, 0, None) != 0
+    L.llc_mfma_loop_data.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    data = ctypes.create_string_buffer(64)
+    base = (ctypes.addressof(data) + 15) // 16 * 16
+    assert L.llc_mfma_loop_data(ctypes.addressof(buf), None, 1, 4, None) != 0       # no operands
+    assert L.llc_mfma_loop_data(ctypes.addressof(buf), base, 1, 6, None) != 0       # iters not a multiple of 4
+    assert L.llc_mfma_loop_data(ctypes.addressof(buf), base + 2, 1, 4, None) != 0   # misaligned operands
+    assert L.llc_mfma_loop_data(None, base, 1, 4, None) != 0
