@@ -84,15 +84,19 @@ def _stats(xs):
 
 
 class ClockSampler:
-    """Reads the GPU's shader clock with amdsmi on a background thread while timed work
-    runs (context manager): the mean over the 8 XCDs of the metrics table's current GFX
-    clocks, kept only while the GFX activity reads >= 90% (the table lags the load by
-    tens of ms).  summary() gives median / min / max in MHz, or why it could not be read."""
+    """Reads the GPU's shader clock and power with amdsmi on a background thread while
+    timed work runs (context manager).  The firmware refreshes its metrics table about
+    once a second, so only fresh tables count (a new firmware timestamp), and only those
+    at least `settle_s` into the window with the GFX activity at >= 90%: each gives the
+    mean over the 8 XCDs of the current GFX clocks and the socket power; the energy
+    counter between the first and the last of them gives the average power.  Windows of
+    two seconds or more give at least one reading.  summary() gives median / min / max
+    in MHz and the power, or why nothing could be read."""
 
-    def __init__(self, period_s=0.01):
-        self.period = period_s
-        self.samples = []
-        self.seen = 0
+    def __init__(self, period_s=0.01, settle_s=0.25):
+        self.period, self.settle = period_s, settle_s
+        self.rows = []           # (clock MHz, socket W, energy uJ, firmware time s)
+        self.fresh = 0
         self.err = None
         self._stop = threading.Event()
         self._th = None
@@ -103,23 +107,27 @@ class ClockSampler:
             if not handles:
                 raise RuntimeError("no GPU handle")
             self._smi, self._h = amdsmi, handles[0]
-            self._read()
+            self._last = self._smi.amdsmi_get_gpu_metrics_info(self._h).get("firmware_timestamp")
         except Exception as e:   # the clock is context; its absence is reported, not fatal
             self.err = f"{type(e).__name__}: {e}"
 
-    def _read(self):
-        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-        clks = [float(c) for c in m.get("current_gfxclks", []) if isinstance(c, (int, float))]
-        act = m.get("average_gfx_activity")
-        return (sum(clks) / len(clks) if clks else None), act
-
     def _loop(self):
+        t0 = time.perf_counter()
         while not self._stop.is_set():
             try:
-                clk, act = self._read()
-                self.seen += 1
-                if clk is not None and isinstance(act, (int, float)) and act >= 90:
-                    self.samples.append(clk)
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                ts = m.get("firmware_timestamp")
+                if ts != self._last:
+                    self._last = ts
+                    self.fresh += 1
+                    clks = [float(c) for c in m.get("current_gfxclks", []) if isinstance(c, (int, float))]
+                    act, pw = m.get("average_gfx_activity"), m.get("current_socket_power")
+                    if (clks and isinstance(act, (int, float)) and act >= 90
+                            and time.perf_counter() - t0 >= self.settle):
+                        e = self._smi.amdsmi_get_energy_count(self._h)
+                        self.rows.append((sum(clks) / len(clks), float(pw) if isinstance(pw, (int, float)) else None,
+                                          e["energy_accumulator"] * e["counter_resolution"],
+                                          ts * 1e-8 if isinstance(ts, int) else None))
             except Exception as e:
                 self.err = f"{type(e).__name__}: {e}"
                 return
@@ -138,16 +146,24 @@ class ClockSampler:
         return False
 
     def summary(self):
-        if not self.samples:
-            return {"error": self.err or f"no sample at >= 90% GFX activity ({self.seen} read)"}
+        if not self.rows:
+            return {"error": self.err or f"no fresh metrics table at >= 90% GFX activity ({self.fresh} fresh)"}
         import numpy as np
-        a = np.asarray(self.samples)
-        return {"median_mhz": float(np.median(a)), "min_mhz": float(a.min()), "max_mhz": float(a.max()),
-                "samples": int(a.size), "source": "amdsmi gpu metrics: mean of the 8 XCDs' current GFX clocks, "
-                                                  "samples at >= 90% GFX activity"}
+        clk = np.asarray([r[0] for r in self.rows])
+        out = {"median_mhz": float(np.median(clk)), "min_mhz": float(clk.min()), "max_mhz": float(clk.max()),
+               "readings": int(clk.size)}
+        pw = [r[1] for r in self.rows if r[1] is not None]
+        if pw:
+            out["socket_w_median"] = float(np.median(pw))
+        (e0, t0), (e1, t1) = self.rows[0][2:], self.rows[-1][2:]
+        if len(self.rows) >= 2 and t0 is not None and t1 is not None and t1 > t0:
+            out["avg_socket_w"] = (e1 - e0) * 1e-6 / (t1 - t0)
+        out["source"] = ("amdsmi: fresh metrics tables (about 1 per second) at >= 90% GFX activity, mean of the "
+                         "8 XCDs' current GFX clocks; socket power; energy counter between the first and last")
+        return out
 
 
-def mfma_ceiling(torch, synth=None, seconds=1.0):
+def mfma_ceiling(torch, synth=None, seconds=2.5):
     """The measured bf16 MFMA ceiling (libllceiling.so): every wave of 8 per CU (two per
     SIMD, as in the attention kernel) issues independent 32x32x16 bf16 MFMAs and nothing
     else.  Launches run back to back for about `seconds`, each timed with events on the
@@ -200,7 +216,7 @@ def mfma_ceiling(torch, synth=None, seconds=1.0):
             else "one operand pair with few mantissa bits set")
     return {"tflops": flop / ms / 1e9, "frac_of_nominal": flop / ms / 1e9 / PEAK_BF16_TFLOPS, "ms": ms,
             "launches": n, "sclk": clk.summary(),
-            "what": "independent 32x32x16 bf16 MFMAs only, 8 waves per CU, sustained (second half of ~1 s); "
+            "what": "independent 32x32x16 bf16 MFMAs only, 8 waves per CU, sustained (second half of ~2.5 s); "
                     + what}
 
 
@@ -252,10 +268,10 @@ def run_steady(torch, ll, synth, cfg, steps, warmup, kv="bf16"):
         step(i, True)
     torch.cuda.synchronize()
     attn_ms = [a0[j].elapsed_time(a1[j]) for j in range(steps * P)]
-    # the shader clock under this attention pass: about one second more of the same
+    # the shader clock under this attention pass: about 2.5 seconds more of the same
     # launches (not part of any figure above) while the clock is sampled
     with ClockSampler() as clk:
-        for i in range(max(1, int(1000.0 / max(sum(attn_ms) / len(attn_ms), 0.01)))):
+        for i in range(max(1, int(2500.0 / max(sum(attn_ms) / len(attn_ms), 0.01)))):
             cache.attn(0, *pool[i % POOL], out)
         torch.cuda.synchronize()
     app_ms = [b0[i].elapsed_time(b1[i]) for i in range(steps)]

@@ -6,6 +6,7 @@ import json
 import os
 import subprocess
 import sys
+import time
 
 import pytest
 
@@ -90,6 +91,37 @@ def test_clock_sampler_reports_rather_than_raises():
         pass
     s = clk.summary()
     assert ("median_mhz" in s) or ("error" in s)
+
+
+def test_clock_sampler_keeps_fresh_tables_only(monkeypatch):
+    """The metrics table refreshes about once a second: repeated reads of one table are
+    one reading, idle tables are dropped, and the average power comes from the energy
+    counter between the first and the last kept table."""
+    import types
+    state = {"reads": 0}
+
+    def metrics(h):
+        state["reads"] += 1
+        k = state["reads"] // 5            # a new table every 5 reads
+        busy = k >= 2                      # the first two tables are idle
+        return {"firmware_timestamp": 1000 + k * 100_000_000, "current_gfxclks": [2000 + k] * 8,
+                "average_gfx_activity": 100 if busy else 0, "current_socket_power": 900 + k}
+
+    def energy(h):
+        k = state["reads"] // 5
+        return {"energy_accumulator": k * 1000, "counter_resolution": 1.0e6, "timestamp": 0}   # 1 kJ per table
+
+    fake = types.SimpleNamespace(amdsmi_init=lambda: None, amdsmi_get_processor_handles=lambda: [0],
+                                 amdsmi_get_gpu_metrics_info=metrics, amdsmi_get_energy_count=energy)
+    monkeypatch.setitem(sys.modules, "amdsmi", fake)
+    clk = bench.ClockSampler(period_s=0.001, settle_s=0.0)
+    with clk:
+        while state["reads"] < 40:
+            time.sleep(0.001)
+    s = clk.summary()
+    assert s["readings"] == clk.fresh - 1 == len(clk.rows), (s, clk.fresh)   # table k = 1 is idle, k = 0 was there before
+    assert s["min_mhz"] == 2002.0 and s["max_mhz"] == 2000 + s["readings"] + 1
+    assert abs(s["avg_socket_w"] - 1000.0) < 1e-6        # 1 kJ per 1 s table step
 
 
 def test_mfma_ceiling_library_exports_its_loop_and_checks_arguments():
