@@ -705,6 +705,9 @@ def main():
                          "JSON record: 30-layer rollout, 400-chunk int8 rollout with recache, "
                          "30-layer recache, window/sink sweep, appends only (warm and cold), the "
                          "steady step with an int8 / fp8 cache at window 21 (for counter runs)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="leave out the measured MFMA ceiling (about 5 s of MFMA-only launches; "
+                         "for counter runs, which time every dispatch)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB "
                          "(reference kernel for scaling HBM byte counters)")
@@ -756,8 +759,8 @@ def main():
     r = run_steady(torch, ll, synth, cfg, args.steps, args.warmup)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     value = cfg.chunk_frames * args.steps / r["wall_s"]
-    ceiling = mfma_ceiling(torch, synth)
-    ceiling_low_bits = mfma_ceiling(torch)
+    ceiling = None if args.no_ceiling else mfma_ceiling(torch, synth)
+    ceiling_low_bits = None if args.no_ceiling else mfma_ceiling(torch)
 
     components = {}
     if not args.no_components:
@@ -814,7 +817,7 @@ def main():
                      "kernel": "attn_kernel (sink+window attention, one pass)",
                      "flop_per_launch": r["attn_flops"], "avg_launch_ms": r["attn_ms"],
                      "median_launch_ms": r["attn_ms_stats"]["median"], "sclk": r["sclk"],
-                     "ceiling": ceiling, "frac_of_ceiling": r["attn_tflops"] / ceiling["tflops"],
+                     "ceiling": ceiling, "frac_of_ceiling": r["attn_tflops"] / ceiling["tflops"] if ceiling else None,
                      "ceiling_low_bits": ceiling_low_bits},
         "attn_tflops": r["attn_tflops"],
         "components": components,

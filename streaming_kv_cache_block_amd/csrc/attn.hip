@@ -56,7 +56,6 @@ constexpr float kLazyThreshold = 8.0f;   // log2 units
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 template <int D, int NW>
 struct Geo {
@@ -64,9 +63,8 @@ struct Geo {
   static constexpr int CH = D / 8;                     // 16-byte chunks per row
   static constexpr int ROWS_PER_DMA = 64 / CH;         // rows one wave-wide 1 KB copy covers
   static constexpr int DMA_PER_WAVE = BN / ROWS_PER_DMA / NW;
-  static constexpr int REG_PASS = BN * CH / NT;        // int8 staging: chunks per thread
   static constexpr int TILE = BN * D;                  // elements per K (or V) tile
-  static_assert(DMA_PER_WAVE >= 1 && REG_PASS >= 1 && NT >= 2 * BN, "tile split");
+  static_assert(DMA_PER_WAVE >= 1 && NT >= 2 * BN, "tile split");
 };
 
 // Swizzled chunk position of chunk c in row r.
