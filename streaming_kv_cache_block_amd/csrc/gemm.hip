@@ -173,41 +173,60 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
       const float a = am[b];
       const bool plain = a < 0x1p-100f || a > 0x1p+120f;
       const float y = 1.0f / a;
+      // codes of values 4 i .. 4 i + 3 of half aa; GEN: any row of the wave may be zero
+      // or outside [2^-100, 2^120] (plain division), else the Markstein path only
+      auto q4 = [&](auto general, int aa, int i) __attribute__((always_inline)) -> uint32_t {
+        constexpr bool GEN = decltype(general)::value;
+        uint32_t packed = 0u;
+        if (!GEN || a > 0.0f) {
+          float qq[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float n = x[b][aa][4 * i + j] * QM;
+            if (GEN && plain) {
+              qq[j] = n / a;
+            } else {
+              qq[j] = n * y;
+              const float r = __builtin_fmaf(-a, qq[j], n);
+              qq[j] = __builtin_fmaf(r, y, qq[j]);
+            }
+          }
+          if constexpr (EPI == 3) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)   // saturate overflowed quotients; keep the sign of zero
+              qq[j] = __builtin_copysignf(fminf(fmaxf(qq[j], -448.0f), 448.0f), x[b][aa][4 * i + j]);
+            packed = f32x2_to_e4m3x2(qq[0], qq[1], 0u, false);
+            packed = f32x2_to_e4m3x2(qq[2], qq[3], packed, true);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int qi = int(fminf(fmaxf(__builtin_rintf(qq[j]), -127.0f), 127.0f));
+              packed |= (uint32_t(qi) & 0xffu) << (8 * j);
+            }
+          }
+        }
+        return packed;
+      };
+      // the test is made once per wave, so that the common case has no branch per value
+      uint32_t pk[2][4];
+      if (__builtin_amdgcn_ballot_w64(plain || !(a > 0.0f)) == 0) {
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk[aa][i] = q4(std::false_type{}, aa, i);
+      } else {
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk[aa][i] = q4(std::true_type{}, aa, i);
+      }
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t packed = 0u;
-          if (a > 0.0f) {
-            float qq[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float n = x[b][aa][4 * i + j] * QM;
-              if (plain) {
-                qq[j] = n / a;
-              } else {
-                qq[j] = n * y;
-                const float r = __builtin_fmaf(-a, qq[j], n);
-                qq[j] = __builtin_fmaf(r, y, qq[j]);
-              }
-            }
-            if constexpr (EPI == 3) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)   // saturate overflowed quotients; keep the sign of zero
-                qq[j] = __builtin_copysignf(fminf(fmaxf(qq[j], -448.0f), 448.0f), x[b][aa][4 * i + j]);
-              packed = f32x2_to_e4m3x2(qq[0], qq[1], 0u, false);
-              packed = f32x2_to_e4m3x2(qq[2], qq[3], packed, true);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int qi = int(fminf(fmaxf(__builtin_rintf(qq[j]), -127.0f), 127.0f));
-                packed |= (uint32_t(qi) & 0xffu) << (8 * j);
-              }
-            }
-          }
           const int n_out = n0 + 64 * wn + 32 * aa + 8 * i + 4 * g;
-          *reinterpret_cast<uint32_t*>(base + srow * N + n_out) = packed;
-          if (srow2 >= 0) *reinterpret_cast<uint32_t*>(base + srow2 * N + n_out) = packed;
+          *reinterpret_cast<uint32_t*>(base + srow * N + n_out) = pk[aa][i];
+          if (srow2 >= 0) *reinterpret_cast<uint32_t*>(base + srow2 * N + n_out) = pk[aa][i];
         }
       const int head = (n0 + 64 * wn) / pc.D;
       if (g == 0 && (pc.D == 64 || (wn & 1) == 0)) {

@@ -150,29 +150,14 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
 
     float scale = 0.0f;
     uint32_t packed[VPL / 4] = {};
-    if (a > 0.0f) {
-      const bool plain = a < 0x1p-100f || a > 0x1p+120f;
-      scale = plain ? a / M : div_by_M<FMT>(a);
-      const float y = plain ? 1.0f / a : rcp_rn_bf16(a);
-      float qq[VPL];
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const float n = x[k] * M;   // exact for bf16 x unless it overflows
-        if (plain) {
-          qq[k] = fminf(fmaxf(n / a, -M), M);
-        } else {
-          qq[k] = n * y;
-          const float r = __builtin_fmaf(-a, qq[k], n);
-          qq[k] = __builtin_fmaf(r, y, qq[k]);
-        }
-      }
+    auto pack = [&](const float (&qq)[VPL]) __attribute__((always_inline)) {
       if constexpr (FMT == kKvFp8) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) qq[k] = __builtin_copysignf(qq[k], x[k]);
-#pragma unroll
         for (int w2 = 0; w2 < VPL / 4; ++w2) {
-          packed[w2] = f32x2_to_e4m3x2(qq[4 * w2], qq[4 * w2 + 1], 0u, false);
-          packed[w2] = f32x2_to_e4m3x2(qq[4 * w2 + 2], qq[4 * w2 + 3], packed[w2], true);
+          packed[w2] = f32x2_to_e4m3x2(__builtin_copysignf(qq[4 * w2], x[4 * w2]),
+                                       __builtin_copysignf(qq[4 * w2 + 1], x[4 * w2 + 1]), 0u, false);
+          packed[w2] = f32x2_to_e4m3x2(__builtin_copysignf(qq[4 * w2 + 2], x[4 * w2 + 2]),
+                                       __builtin_copysignf(qq[4 * w2 + 3], x[4 * w2 + 3]), packed[w2], true);
         }
       } else {
         uint32_t t[VPL];
@@ -183,6 +168,40 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
           packed[j] = __builtin_amdgcn_perm(t[4 * j + 1], t[4 * j], 0x0c0c0400u) |
                       __builtin_amdgcn_perm(t[4 * j + 3], t[4 * j + 2], 0x04000c0cu);
       }
+    };
+    // Rows whose absmax is zero or outside [2^-100, 2^120] take plain divisions; the
+    // test is made once per wave, so that the common case runs without a branch per
+    // value (the per-lane form compiled to an exec-masked branch around each value).
+    const bool plain = !(a >= 0x1p-100f && a <= 0x1p+120f);
+    if (__builtin_amdgcn_ballot_w64(plain) == 0) {
+      scale = div_by_M<FMT>(a);
+      const float y = rcp_rn_bf16(a);
+      float qq[VPL];
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        const float n = x[k] * M;   // exact for bf16 x
+        const float q0 = n * y;
+        const float r = __builtin_fmaf(-a, q0, n);
+        qq[k] = __builtin_fmaf(r, y, q0);
+      }
+      pack(qq);
+    } else if (a > 0.0f) {
+      const bool pl = a < 0x1p-100f || a > 0x1p+120f;
+      scale = pl ? a / M : div_by_M<FMT>(a);
+      const float y = pl ? 1.0f / a : rcp_rn_bf16(a);
+      float qq[VPL];
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        const float n = x[k] * M;   // exact for bf16 x unless it overflows
+        if (pl) {
+          qq[k] = fminf(fmaxf(n / a, -M), M);
+        } else {
+          qq[k] = n * y;
+          const float r = __builtin_fmaf(-a, qq[k], n);
+          qq[k] = __builtin_fmaf(r, y, qq[k]);
+        }
+      }
+      pack(qq);
     }
     if (row < p.rows_per_frame) {
 #pragma unroll
