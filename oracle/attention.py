@@ -26,6 +26,7 @@ accumulation (numpy BLAS), or float64 for the pins.
 import numpy as np
 
 from . import bf16 as _bf16
+from . import mxfp4 as _mx
 from . import quant as _quant
 from . import visibility as _vis
 
@@ -105,10 +106,11 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
     history(f) -> (K_f, V_f): uint16 bf16 bits [T][H][D], the K/V that frame
         f had when it entered the cache (or the recache tensor that replaced
         it).  Only frames in V(f0) are requested.
-    kv: cache format "bf16" (default), "int8" or "fp8": for the last two the
-        cached frames pass through the per-(token, head) absmax rule of that
-        format (oracle.quant) and are dequantised before use; own-chunk K/V
-        are never quantised.  kv_int8=True is the same as kv="int8".
+    kv: cache format "bf16" (default), "int8", "fp8" or "mxfp4": for the
+        low-bit formats the cached frames pass through that format's rule
+        (oracle.quant: per-(token, head) absmax; oracle.mxfp4: per block of 32
+        values) and are dequantised before use; own-chunk K/V are never
+        quantised.  kv_int8=True is the same as kv="int8".
     rows: optional list of query rows to compute (sampled checks).
     shot: optional (Ss, fs): a shot sink of the first Ss frames of the shot that
         starts at frame fs (visibility.visible_frames_shots).
@@ -121,7 +123,7 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
     """
     if kv is None:
         kv = "int8" if kv_int8 else "bf16"
-    if kv not in ("bf16", "int8", "fp8"):
+    if kv not in ("bf16", "int8", "fp8", "mxfp4"):
         raise ValueError(f"unknown cache format {kv!r}")
     T = tokens_per_frame
     nq_all, H, D = Q.shape
@@ -146,6 +148,9 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
             elif kv == "fp8":
                 Ks.append(_quant.dequantize_fp8(*_quant.quantize_fp8(_bf16.to_f32(kf))).astype(dtype))
                 Vs.append(_quant.dequantize_fp8(*_quant.quantize_fp8(_bf16.to_f32(vf))).astype(dtype))
+            elif kv == "mxfp4":
+                Ks.append(_mx.dequantize(*_mx.quantize(_bf16.to_f32(kf))).astype(dtype))
+                Vs.append(_mx.dequantize(*_mx.quantize(_bf16.to_f32(vf))).astype(dtype))
             else:
                 Ks.append(_widen(kf, dtype))
                 Vs.append(_widen(vf, dtype))
