@@ -216,6 +216,73 @@ struct QTile {
   }
 };
 
+// MXFP4 cache tile (E2M1 codes, one E8M0 scale per block of 32 values of a row;
+// LongLive-2.0 explainer, wmrh.cn, §15.3: the 4-bit history cache dequantised in
+// parallel where it is used).  Staged like the tiles above, two tiles ahead: a row
+// is D/2 code bytes, so one wave-wide copy moves ROWS rows of one operand, and the
+// waves share the 2 * COPIES copies of a tile (K copies first, then V).  Each lane's
+// 16 staged bytes are one block; the hardware's scaled conversion turns two codes and
+// the block's power-of-two scale into two bf16 values in one instruction, exactly
+// (every value(q) * 2^e of the format is a bf16 value), for K as for V.  The widened
+// tile is an ordinary bf16 tile: no per-key factors, the bf16 softmax and P*V.
+template <int D, int NW>
+struct QTile4 {
+  static constexpr int RB = D / 2;                   // code bytes per row
+  static constexpr int CH4 = RB / 16;                // 16-byte chunks (= blocks) per row
+  static constexpr int ROWS = 64 / CH4;              // rows per wave-wide 1 KB copy
+  static constexpr int COPIES = BN / ROWS;           // copies per operand per tile
+  static constexpr int ITER = 2 * COPIES / NW;       // copies per wave (K and V together)
+  static constexpr int STAGE = BN * RB;              // code bytes per operand
+  static constexpr int SCALES = 2 * COPIES * 64;     // staged scale words: 64 per copy
+  static constexpr int OPS = 2 * ITER;               // vector-memory instructions of issue()
+  static_assert(ITER >= 1 && (2 * COPIES) % NW == 0 && ROWS <= 64, "every wave copies whole copies");
+
+  __device__ static void issue(const AttnParams& p, int h, const TileInfo& ti, int8_t* stage, float* sst,
+                               int wave, int lane) {
+    const int64_t rs = int64_t(p.H) * RB;
+    const int64_t base = int64_t(ti.start) * rs + int64_t(h) * RB;
+    const int64_t sbase = int64_t(ti.start) * p.H + h;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int i = wave + it * NW;
+      const bool isv = i >= COPIES;
+      const int r0 = (i % COPIES) * ROWS;
+      const int8_t* g = static_cast<const int8_t*>(isv ? p.cV : p.cK) + base;
+      // rows past the end re-read the last one (masked to -inf, finite data)
+      const uint32_t off = uint32_t(int64_t(min(r0 + lane / CH4, ti.cnt - 1)) * rs + 16 * (lane % CH4));
+      copy_lds<16>(g, off, stage + (isv ? STAGE : 0) + r0 * RB);
+      // scale words: lane t of the copy takes row r0 + t % ROWS
+      const uint32_t soff = uint32_t(min(r0 + lane % ROWS, ti.cnt - 1) * p.H * 4);
+      copy_lds<4>((isv ? p.cVs : p.cKs) + sbase, soff, sst + i * 64);
+    }
+  }
+
+  // Called by the same wave once its copies of the tile have landed.
+  __device__ static void widen(const int8_t* stage, const float* sst, uint16_t* lk, uint16_t* lv, float*, float,
+                               int wave, int lane) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int i = wave + it * NW;
+      const bool isv = i >= COPIES;
+      const int rl = lane / CH4, blk = lane % CH4;
+      const int r = (i % COPIES) * ROWS + rl;
+      const u32x4 q = *reinterpret_cast<const u32x4*>(stage + (isv ? STAGE : 0) + r * RB + 16 * blk);
+      const uint32_t word = __builtin_bit_cast(uint32_t, sst[i * 64 + rl]);
+      const float sc = __builtin_bit_cast(float, ((word >> (8 * blk)) & 0xFFu) << 23);   // 2^e
+      uint16_t* dst = (isv ? lv : lk) + r * D;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 v = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[k], sc, 0)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[k], sc, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[k], sc, 2)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[k], sc, 3))};
+        *reinterpret_cast<u32x4*>(dst + 8 * swz<D>(r, 4 * blk + k)) = v;
+      }
+    }
+  }
+};
+
 // Wait until at most N vector-memory instructions of this wave are in flight (they
 // complete in issue order).
 // (The builtin, not inline asm: the compiler's own wait placement then knows what has
@@ -765,10 +832,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   __shared__ __attribute__((aligned(1024))) uint16_t sm_k1[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v0[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v1[G::TILE];
-  constexpr bool KV8 = KVQ != kKvBf16;   // quantised cache (int8 or fp8 codes)
-  using QT = QTile<D, NW, KVQ>;
-  __shared__ __attribute__((aligned(16))) float sm_kf0[KV8 ? BN : 1];   // per-key score factors
-  __shared__ __attribute__((aligned(16))) float sm_kf1[KV8 ? BN : 1];
+  constexpr bool KV8 = KVQ != kKvBf16;   // quantised cache (int8, fp8 or fp4 codes), staged tiles
+  constexpr bool KSC = KVQ == kKvInt8 || KVQ == kKvFp8;   // per-row scales: per-key score factors
+  using QT = std::conditional_t<KVQ == kKvMxfp4, QTile4<D, NW>, QTile<D, NW, KVQ>>;
+  __shared__ __attribute__((aligned(16))) float sm_kf0[KSC ? BN : 1];   // per-key score factors
+  __shared__ __attribute__((aligned(16))) float sm_kf1[KSC ? BN : 1];
   __shared__ __attribute__((aligned(1024))) int8_t sm_stage0[KV8 ? 2 * QT::STAGE : 16];   // K, V codes
   __shared__ __attribute__((aligned(1024))) int8_t sm_stage1[KV8 ? 2 * QT::STAGE : 16];
   __shared__ __attribute__((aligned(16))) float sm_sst0[KV8 ? QT::SCALES : 1];            // their scales
@@ -875,13 +943,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
         }
       };
       constexpr bool MASK = MODE == 0;
-      constexpr bool SC = MODE == 1 || (MODE == 0 && KV8);
+      constexpr bool SC = KSC && (MODE == 1 || MODE == 0);
       int cnt = BN;
       bool scaled = SC;
       if constexpr (MODE == 0) {
         const TileInfo t = order.at(j);
         cnt = t.cnt;
-        scaled = KV8 && t.seg == 0;
+        scaled = KSC && t.seg == 0;
       }
       A.template tile<MASK, SC>(PB ? sm_k1 : sm_k0, PB ? sm_v1 : sm_v0, PB ? sm_kf1 : sm_kf0, cnt, scaled, mid);
       // everything this wave copied (the next tile, the codes two tiles ahead) has
@@ -1008,12 +1076,14 @@ hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t 
       case kKvBf16: return big ? launch_t<128, 1, 8, kKvBf16>(p, s) : launch_t<128, 1, 4, kKvBf16>(p, s);
       case kKvInt8: return big ? launch_t<128, 1, 8, kKvInt8>(p, s) : launch_t<128, 1, 4, kKvInt8>(p, s);
       case kKvFp8: return big ? launch_t<128, 1, 8, kKvFp8>(p, s) : launch_t<128, 1, 4, kKvFp8>(p, s);
+      case kKvMxfp4: return big ? launch_t<128, 1, 8, kKvMxfp4>(p, s) : launch_t<128, 1, 4, kKvMxfp4>(p, s);
     }
   } else if (D == 64) {
     switch (kv_fmt) {
       case kKvBf16: return big ? launch_t<64, 2, 4, kKvBf16>(p, s) : launch_t<64, 1, 4, kKvBf16>(p, s);
       case kKvInt8: return big ? launch_t<64, 2, 4, kKvInt8>(p, s) : launch_t<64, 1, 4, kKvInt8>(p, s);
       case kKvFp8: return big ? launch_t<64, 2, 4, kKvFp8>(p, s) : launch_t<64, 1, 4, kKvFp8>(p, s);
+      case kKvMxfp4: return big ? launch_t<64, 2, 4, kKvMxfp4>(p, s) : launch_t<64, 1, 4, kKvMxfp4>(p, s);
     }
   }
   return hipErrorInvalidValue;

@@ -1,7 +1,8 @@
 // cache.cpp -- the C ABI: cache handle, host bookkeeping, validation, kernel dispatch.
 //
 // The handle owns one device allocation holding, per layer, the K and V slot arrays
-// [S+W][T][H][D] (bf16, int8 or fp8), for int8 / fp8 their [S+W][T][H] fp32 scales,
+// [S+W][T][H][D] (bf16, int8 or fp8; MXFP4 [S+W][T][H][D/2] bytes), for the low-bit
+// caches their [S+W][T][H] scales (fp32, or for MXFP4 words of E8M0 block-scale bytes),
 // and the attention work area of the split key walk (partials and counters).  Host
 // bookkeeping per layer: frames seen (f0) and the frame held by each slot.  Every
 // argument is checked before the first HIP call so that errors are testable on a
@@ -254,6 +255,9 @@ __global__ void poison_kernel(uint32_t* p, int64_t n_words, uint32_t pattern) {
     p[i] = pattern;
 }
 
+// Scale words of a poisoned slot: fp32 NaN (int8 / fp8), or E8M0 NaN bytes (MXFP4).
+uint32_t scale_poison(int kv_dtype) { return kv_dtype == LL_KV_MXFP4 ? 0xFFFFFFFFu : 0x7FC00000u; }
+
 hipError_t poison(void* p, size_t bytes, uint32_t pattern, hipStream_t s) {
   const int64_t words = int64_t(bytes / 4);
   if (words == 0) return hipSuccess;
@@ -272,9 +276,10 @@ ll_status poison_planned(ll_cache* c, int layer, const std::vector<ll::WriteEntr
       if (e == hipSuccess)
         e = poison(static_cast<char*>(c->v(layer)) + size_t(w.slot) * slot_vals * 2, slot_vals * 2, 0x7FC07FC0u, s);
     } else {
-      e = poison(c->ks(layer) + size_t(w.slot) * size_t(c->rows_per_frame), size_t(c->rows_per_frame) * 4, 0x7FC00000u, s);
+      const uint32_t pat = scale_poison(c->kv_dtype);
+      e = poison(c->ks(layer) + size_t(w.slot) * size_t(c->rows_per_frame), size_t(c->rows_per_frame) * 4, pat, s);
       if (e == hipSuccess)
-        e = poison(c->vs(layer) + size_t(w.slot) * size_t(c->rows_per_frame), size_t(c->rows_per_frame) * 4, 0x7FC00000u, s);
+        e = poison(c->vs(layer) + size_t(w.slot) * size_t(c->rows_per_frame), size_t(c->rows_per_frame) * 4, pat, s);
     }
     if (e != hipSuccess) return hip_fail(e, "poisoning slots before a rewrite");
   }
@@ -307,14 +312,15 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
   const int64_t slots = int64_t(sink_frames) + shot_sink_frames + window_frames;
   if (slots < 1 || slots > LL_MAX_SLOTS)
     return fail(LL_ERR_INVALID, "sink_frames + shot_sink_frames + window_frames must be in [1, %d]", LL_MAX_SLOTS);
-  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8 && kv_dtype != LL_KV_FP8)
+  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8 && kv_dtype != LL_KV_FP8 && kv_dtype != LL_KV_MXFP4)
     return fail(LL_ERR_INVALID, "unknown kv_dtype %d", kv_dtype);
   const int64_t rows = int64_t(tokens_per_frame) * heads;
   if (slots * tokens_per_frame > kMaxRows || rows > kMaxRows) return fail(LL_ERR_INVALID, "cache too large");
   const bool quantised = kv_dtype != LL_KV_BF16;
-  const int64_t elt = quantised ? 1 : 2;
+  // code bytes per (token, head) row: 2 per value (bf16), 1 (int8, fp8) or 1/2 (MXFP4)
+  const int64_t row_bytes = kv_dtype == LL_KV_BF16 ? 2 * head_dim : kv_dtype == LL_KV_MXFP4 ? head_dim / 2 : head_dim;
   auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
-  const int64_t kv_bytes = round256(slots * rows * head_dim * elt);
+  const int64_t kv_bytes = round256(slots * rows * row_bytes);
   const int64_t sc_bytes = quantised ? round256(slots * rows * 4) : 0;
   const double cache_total = double(layers) * 2.0 * double(kv_bytes + sc_bytes);
   if (cache_total > double(int64_t(1) << 46)) return fail(LL_ERR_INVALID, "cache too large (%.3g bytes)", cache_total);
@@ -350,7 +356,7 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
     if (e == hipSuccess) {   // every slot poisoned: bf16 NaN codes, or NaN scales
       if (!quantised) e = poison(mem, size_t(layers) * 2 * size_t(kv_bytes), 0x7FC07FC0u, zs);
       else e = poison(static_cast<char*>(mem) + size_t(layers) * 2 * size_t(kv_bytes), size_t(layers) * 2 * size_t(sc_bytes),
-                      0x7FC00000u, zs);
+                      scale_poison(kv_dtype), zs);
     }
 #endif
     if (e == hipSuccess) {
@@ -538,6 +544,8 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
     return fail(LL_ERR_INVALID, "heads*head_dim = %lld must be a multiple of 128", (long long)d_out);
   const int64_t f0 = c->f0[size_t(layer)];
   const int64_t fs = c->fs[size_t(layer)];
+  if (c->kv_dtype == LL_KV_MXFP4)
+    return fail(LL_ERR_INVALID, "recache_from_hidden: MXFP4 caches take ll_kv_project + ll_cache_recache");
   const int64_t need = ll::cached_frames(f0, c->layout(), fs);
   if (need == 0) return fail(LL_ERR_STATE, "recache_from_hidden: layer %d holds no frames", layer);
   if (n_frames != need)

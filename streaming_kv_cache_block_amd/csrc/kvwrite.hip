@@ -19,7 +19,8 @@
 // OCP E4M3 value) and the quotient, clamped to [-448, 448] (it exceeds that only when
 // x * 448 overflowed), rounded to E4M3 (nearest, ties to even) by the hardware
 // conversion.  LongLive-2.0 explainer, wmrh.cn, §15.2: the history cache is
-// stored in low precision to save memory and traffic.
+// stored in low precision to save memory and traffic.  MXFP4 caches: see
+// mx4_frames_kernel.
 #include "device_common.h"
 #include "launch.h"
 
@@ -213,6 +214,81 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
   }
 }
 
+// MXFP4 caches (OCP MX: E2M1 codes, one E8M0 power-of-two scale per block of 32
+// values; LongLive-2.0 explainer, wmrh.cn, §15.2: the history cache in 4-bit floating
+// point).  Same lane layout as the quantising writes above: D/16 lanes per (token,
+// head) row, 16 consecutive values per lane, so a block of 32 is a lane pair.  Per
+// block: a = max |x| (lane pair, one DPP swap), e = max(floor(log2 a) - 2, -125) read
+// off a's exponent field (a bf16 value; 0 and subnormals give -125), y = x * 2^-e (exact),
+// and the hardware conversion to E2M1 with unit scale: nearest, ties to the even code,
+// saturating at 6, sign kept (checked against the format definition for every
+// midpoint, the saturation range and signed zeros).  A lane's 16 codes (8 bytes, value
+// 2k in the low half of byte k) leave with one 8-byte store; the first lane of a row
+// gathers the row's block exponents into one scale word (byte b = e_b + 127).
+template <int D>
+__global__ __launch_bounds__(kThreads) void mx4_frames_kernel(const WriteParams p) {
+  constexpr int VPL = kQuantValues;
+  constexpr int LPR = D / VPL;
+  constexpr int GROUPS = kThreads / LPR;
+  constexpr int RPG = kQuantRows;
+  static_assert(VPL == 16 && (LPR == 4 || LPR == 8), "a block of 32 values is a lane pair");
+  const int e = blockIdx.y;
+  const bool isv = blockIdx.z != 0;
+  const int sub = threadIdx.x % LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = (int64_t(blockIdx.x) * GROUPS + threadIdx.x / LPR) * RPG;
+  const uint16_t* src = (isv ? p.srcV : p.srcK) + int64_t(p.plan_src[e]) * p.rows_per_frame * D;
+  uint8_t* dst = static_cast<uint8_t*>(isv ? p.dstV : p.dstK) + int64_t(p.plan_slot[e]) * p.rows_per_frame * (D / 2);
+  uint32_t* dsc = reinterpret_cast<uint32_t*>(isv ? p.dstVs : p.dstKs) + int64_t(p.plan_slot[e]) * p.rows_per_frame;
+
+  u32x4 w[RPG][VPL / 8];
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) {
+    const int64_t row = row0 + rr;
+#pragma unroll
+    for (int h = 0; h < VPL / 8; ++h)
+      w[rr][h] = row < p.rows_per_frame ? *reinterpret_cast<const u32x4*>(src + row * D + VPL * sub + 8 * h)
+                                        : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) {
+    const int64_t row = row0 + rr;
+    float x[VPL];
+#pragma unroll
+    for (int h = 0; h < VPL / 8; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * h + 2 * k] = __builtin_bit_cast(float, w[rr][h][k] << 16);
+        x[8 * h + 2 * k + 1] = __builtin_bit_cast(float, w[rr][h][k] & 0xffff0000u);
+      }
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) a = fmaxf(a, fabsf(x[k]));
+    a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false)));
+    const int eb = max(int(__builtin_bit_cast(uint32_t, a) >> 23) - 129, -125);
+    const float inv = __builtin_bit_cast(float, uint32_t(127 - eb) << 23);   // 2^-e, a normal float
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h] * inv, x[8 * h + 1] * inv, 1.0f, 0);
+      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 2] * inv, x[8 * h + 3] * inv, 1.0f, 1);
+      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 4] * inv, x[8 * h + 5] * inv, 1.0f, 2);
+      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 6] * inv, x[8 * h + 7] * inv, 1.0f, 3);
+    }
+    // scale word of the row: block b's byte comes from lane sub = 2 b of the row
+    const int byte = eb + 127;
+    uint32_t word = uint32_t(byte);
+#pragma unroll
+    for (int b = 1; b < D / 32; ++b)
+      word |= uint32_t(__builtin_amdgcn_ds_bpermute(4 * ((lane + 2 * b) & 63), byte)) << (8 * b);
+    if (row < p.rows_per_frame) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store(u32x2{c[0], c[1]}, reinterpret_cast<u32x2*>(dst + row * (D / 2) + 8 * sub));
+      if (sub == 0) dsc[row] = word;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t s) {
@@ -226,6 +302,12 @@ hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t 
   }
   const int rows_per_block = kThreads / (D / kQuantValues) * kQuantRows;
   dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
+  if (kv_fmt == kKvMxfp4) {
+    if (D == 128) hipLaunchKernelGGL(mx4_frames_kernel<128>, grid, dim3(kThreads), 0, s, p);
+    else if (D == 64) hipLaunchKernelGGL(mx4_frames_kernel<64>, grid, dim3(kThreads), 0, s, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (D == 128 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<128, kKvInt8>), grid, dim3(kThreads), 0, s, p);
   else if (D == 64 && kv_fmt == kKvInt8) hipLaunchKernelGGL((quant_frames_kernel<64, kKvInt8>), grid, dim3(kThreads), 0, s, p);
   else if (D == 128 && kv_fmt == kKvFp8) hipLaunchKernelGGL((quant_frames_kernel<128, kKvFp8>), grid, dim3(kThreads), 0, s, p);

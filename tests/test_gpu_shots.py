@@ -119,6 +119,14 @@ def test_shot_rollout_with_recache(torch_gpu, kv, S, Ss, W, T, D):
              recache_at=(5, 9), fused_recache_at=(7, 12))
 
 
+@pytest.mark.parametrize("S,Ss,W,T,D", [(3, 3, 6, 16, 64), (1, 4, 5, 33, 128)])
+def test_shot_rollout_with_recache_mxfp4(torch_gpu, S, Ss, W, T, D):
+    """As above for an MXFP4 cache, whose recaches all go through ll_cache_recache (the
+    fused projection epilogue takes bf16, int8 and fp8 caches only)."""
+    _log(f"shots kv=mxfp4 S={S} Ss={Ss} W={W} T={T} D={D}")
+    _rollout(torch_gpu, S, Ss, W, T, 2, D, "mxfp4", seed=760 + S * 10 + Ss, recache_at=(5, 7, 9, 12))
+
+
 def test_shot_rollout_full_shape(torch_gpu):
     """12 heads x 128, 1560 tokens per frame: three cache runs at full size (the
     one-workgroup-per-CU split walk), sampled rows."""
