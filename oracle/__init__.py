@@ -30,10 +30,11 @@ Modules
                (append/evict, recache rewrite) used to check cache bytes.
 ``quant``      int8 and fp8 per-(token, head) absmax quantisation and dequantisation.
 ``mxfp4``      4-bit E2M1 codes with a power-of-two scale per block of 32 values.
+``mxfp8``      E4M3 codes with a power-of-two scale per block of 32 values.
 ``gemm``       the recache projection K = W_K h (row form) rounded to bf16.
 
 Every function states the passage it follows.  Parity status of each part
 (pinned or not) is listed in the tests that pin it; no part is unpinned.
 """
 
-from . import bf16, visibility, attention, ring, quant, mxfp4, gemm  # noqa: F401
+from . import bf16, visibility, attention, ring, quant, mxfp4, mxfp8, gemm  # noqa: F401

@@ -27,6 +27,7 @@ import numpy as np
 
 from . import bf16 as _bf16
 from . import mxfp4 as _mx
+from . import mxfp8 as _mx8
 from . import quant as _quant
 from . import visibility as _vis
 
@@ -106,11 +107,11 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
     history(f) -> (K_f, V_f): uint16 bf16 bits [T][H][D], the K/V that frame
         f had when it entered the cache (or the recache tensor that replaced
         it).  Only frames in V(f0) are requested.
-    kv: cache format "bf16" (default), "int8", "fp8" or "mxfp4": for the
-        low-bit formats the cached frames pass through that format's rule
-        (oracle.quant: per-(token, head) absmax; oracle.mxfp4: per block of 32
-        values) and are dequantised before use; own-chunk K/V are never
-        quantised.  kv_int8=True is the same as kv="int8".
+    kv: cache format "bf16" (default), "int8", "fp8", "mxfp4" or "mxfp8": for
+        the low-bit formats the cached frames pass through that format's rule
+        (oracle.quant: per-(token, head) absmax; oracle.mxfp4 / oracle.mxfp8:
+        per block of 32 values) and are dequantised before use; own-chunk K/V
+        are never quantised.  kv_int8=True is the same as kv="int8".
     rows: optional list of query rows to compute (sampled checks).
     shot: optional (Ss, fs): a shot sink of the first Ss frames of the shot that
         starts at frame fs (visibility.visible_frames_shots).
@@ -123,7 +124,7 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
     """
     if kv is None:
         kv = "int8" if kv_int8 else "bf16"
-    if kv not in ("bf16", "int8", "fp8", "mxfp4"):
+    if kv not in ("bf16", "int8", "fp8", "mxfp4", "mxfp8"):
         raise ValueError(f"unknown cache format {kv!r}")
     T = tokens_per_frame
     nq_all, H, D = Q.shape
@@ -151,6 +152,9 @@ def chunk_attention(Q, K_chunk, V_chunk, history, f0, S, W, tokens_per_frame,
             elif kv == "mxfp4":
                 Ks.append(_mx.dequantize(*_mx.quantize(_bf16.to_f32(kf))).astype(dtype))
                 Vs.append(_mx.dequantize(*_mx.quantize(_bf16.to_f32(vf))).astype(dtype))
+            elif kv == "mxfp8":
+                Ks.append(_mx8.dequantize(*_mx8.quantize(_bf16.to_f32(kf))).astype(dtype))
+                Vs.append(_mx8.dequantize(*_mx8.quantize(_bf16.to_f32(vf))).astype(dtype))
             else:
                 Ks.append(_widen(kf, dtype))
                 Vs.append(_widen(vf, dtype))

@@ -185,3 +185,126 @@ def test_mxfp4_attention_worked_example():
     }
     for name, alt in planted.items():
         assert np.abs(alt - want).max() > 1e-4, name
+
+
+# ---- MXFP8: E4M3 elements (oracle.quant's rounding, pinned against torch's
+# float8_e4m3fn there) with the same power-of-two block scale ----------------------
+
+def test_mxfp8_block_exponent_closed_forms():
+    from oracle import mxfp8
+    # e = floor(log2 a) - 8, at least -117 (a = 0 gives -117)
+    cases = {1.0: -8, 256.0: 0, 255.5: -1, 448.0: 0, 511.0: 0, 512.0: 1, 0.3: -10,
+             0.0: -117, 2.0 ** -115: -117, 2.0 ** -109: -117, 2.0 ** -108: -116,
+             1.5 * 2.0 ** 127: 119}
+    for a, e in cases.items():
+        x = np.zeros(32)
+        x[3] = a
+        assert mxfp8.block_exponents(x)[0] == e, a
+
+
+def test_mxfp8_grid_values_exact_saturation_and_error_bound():
+    from oracle import mxfp8, quant
+    rng = np.random.default_rng(8)
+    vals = quant.e4m3_values()                       # 127 non-negative finite values
+    n = 400
+    k = rng.integers(-30, 30, size=(n, 4))
+    mags = vals[rng.integers(0, 127, size=(n, 4, 32))]
+    mags[..., 0] = vals[rng.integers(120, 127, size=(n, 4))]   # block max in [256, 448]
+    x = (mags * rng.choice([-1.0, 1.0], size=mags.shape) * np.ldexp(1.0, k)[..., None]).reshape(n, 128)
+    codes, e = mxfp8.quantize(x.astype(np.float32))
+    assert np.array_equal(e, k)
+    assert np.array_equal(mxfp8.dequantize(codes, e).astype(np.float64), x)
+    # saturation: a block max of 480 * 2^k (a / 2^e in [256, 512)) comes back as 448 * 2^k
+    y = np.zeros((1, 32))
+    y[0, :3] = [480.0, -500.0, 300.0]
+    c, ee = mxfp8.quantize(y.astype(np.float32))
+    assert ee[0, 0] == 0 and list(mxfp8.dequantize(c, ee)[0, :3]) == [448.0, -448.0, 288.0]
+    # half-step error bound on Gaussian bf16 rows, and bf16-exact dequantised values
+    xg = bf16.to_f32(synth.normal_bf16((2000, 128), 1.0, 9, 0))
+    cg, eg = mxfp8.quantize(xg)
+    xh = mxfp8.dequantize(cg, eg).astype(np.float64)
+    assert np.array_equal(bf16.to_f32(bf16.round_f32(xh.astype(np.float32))), xh)
+    X = np.repeat(np.ldexp(1.0, eg), 32, axis=-1)
+    ay = np.abs(xg.astype(np.float64)) / X
+    # E4M3 spacing at |y| in [2^j, 2^(j+1)) is 2^(j-3) (normal), 2^-9 below 2^-6
+    j = np.floor(np.log2(np.maximum(ay, 2.0 ** -6)))
+    half = np.where(ay <= 448.0, 2.0 ** (j - 4), ay - 448.0)
+    assert np.all(np.abs(xg - xh) <= half * X)
+    # signed zero and values that round to zero keep their sign
+    z = np.zeros((1, 32), dtype=np.float32)
+    z[0, 0], z[0, 1], z[0, 2] = 1.0, -0.0, -2.0 ** -20
+    cz, _ = mxfp8.quantize(z)
+    assert cz[0, 1] == 0x80 and cz[0, 2] == 0x80 and cz[0, 3] == 0x00
+
+
+def test_mxfp8_attention_equals_bf16_when_exact_and_worked_example():
+    """Exactly quantisable history rows give the bf16 result bit for bit (own chunk
+    generic, so it is used as given); and a hand-worked case: D = 32, one block with
+    448 in a dim the query ignores (e = floor(log2 448) - 8 = 0, scale 1), entries
+    rounded by hand to E4M3, ties to the even code: K 1.0625 -> 1, 1.1875 -> 1.25;
+    V 3.125 -> 3, -5.25 -> -5; K or V unquantised, or the own chunk quantised, each move
+    the closed form far outside the tolerance."""
+    from oracle import mxfp8, quant
+    C, T, H, D, S, W = 3, 16, 2, 64, 3, 6
+    rng = np.random.default_rng(44)
+    vals = quant.e4m3_values()
+
+    def exact(n):
+        k = rng.integers(-6, 3, size=(n, H, D // 32))
+        mags = vals[rng.integers(0, 127, size=(n, H, D // 32, 32))]
+        mags[..., 0] = 448.0
+        x = mags * rng.choice([-1.0, 1.0], size=mags.shape) * np.ldexp(1.0, k)[..., None]
+        bits = bf16.round_f32(x.reshape(n, H, D).astype(np.float32))
+        assert (bf16.to_f32(bits).astype(np.float64) == x.reshape(n, H, D)).all()
+        return bits
+
+    kh, vh = exact(12 * T), exact(12 * T)
+    hist = lambda f: (kh[f * T:(f + 1) * T], vh[f * T:(f + 1) * T])
+    for f0 in (0, 3, 9, 12):
+        q, kc, vc = (synth.normal_bf16((C * T, H, D), 1.0, 45, f0, t) for t in range(3))
+        assert (mxfp8.dequantize(*mxfp8.quantize(bf16.to_f32(kc))) != bf16.to_f32(kc)).any()
+        a = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv="mxfp8")
+        b = attention.chunk_attention(q, kc, vc, hist, f0, S, W, T, kv="bf16")
+        assert np.array_equal(a, b), f0
+
+    Dw = 32
+
+    def row(entries):
+        r = [0.0] * Dw
+        for d, v in entries.items():
+            r[d] = v
+        return r
+
+    K_in = [row({0: 1.0625, 5: 448.0}), row({0: 1.1875, 5: -448.0})]
+    K_hat = [row({0: 1.0, 5: 448.0}), row({0: 1.25, 5: -448.0})]
+    V_in = [row({0: 3.125, 6: 448.0}), row({0: -5.25, 6: -448.0})]
+    V_hat = [row({0: 3.0, 6: 448.0}), row({0: -5.0, 6: -448.0})]
+    own_k = [row({0: 1.0})]
+    own_v = [row({0: 0.5, 1: 0.3125, 2: -0.75})]   # block max 0.75: e = -9, 0.3125 * 512 = 160 exact
+    own_v2 = [row({0: 0.5, 1: 0.30078125, 2: -0.75})]  # y = 154: MXFP8 would change it
+    q = [row({0: 2.0})]
+    as_bits = lambda rows: bf16.round_f32(np.array(rows, dtype=np.float32).reshape(len(rows), 1, Dw))
+    kb, vb = as_bits(K_in), as_bits(V_in)
+    hist1 = lambda f: (kb[f:f + 1], vb[f:f + 1])
+    got = attention.chunk_attention(as_bits(q), as_bits(own_k), as_bits(own_v2), hist1, 2, 1, 1, 1,
+                                    kv="mxfp8", dtype=np.float64)[0, 0]
+    sc = 1.0 / math.sqrt(Dw)
+
+    def closed_form(keys, vals_):
+        s = [sum(qi * ki for qi, ki in zip(q[0], k)) * sc for k in keys]
+        e = [math.exp(x - max(s)) for x in s]
+        return np.array([sum(e[j] * vals_[j][d] for j in range(3)) / sum(e) for d in range(Dw)])
+
+    want = closed_form(K_hat + own_k, V_hat + own_v2)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # own V through MXFP8 by hand: block max 0.75 -> e = floor(log2 0.75) - 8 = -9,
+    # y = x * 512: 0.30078125 -> 154; E4M3 spacing in [128, 256) is 16, so the neighbours
+    # are 144 and 160 and 154 rounds to 160 -> 160 / 512 = 0.3125
+    own_vq = [row({0: 0.5, 1: 0.3125, 2: -0.75})]
+    planted = {
+        "K unquantised": closed_form(K_in + own_k, V_hat + own_v2),
+        "V unquantised": closed_form(K_hat + own_k, V_in + own_v2),
+        "own chunk quantised": closed_form(K_hat + own_k, V_hat + own_vq),
+    }
+    for name, alt in planted.items():
+        assert np.abs(alt - want).max() > 1e-4, name
