@@ -10,7 +10,7 @@ sets, one per pass, reused cyclically across steps).
 
 Prints ONE JSON line with the whole-step throughput in latent frames/s per layer,
 the attention kernel's roofline position, component timings (per-kernel median /
-p10 / p90; int8, fp8 and mxfp4 caches; warm and cold appends; the 30-layer rollout, the
+p10 / p90; int8, fp8, mxfp4 and mxfp8 caches; warm and cold appends; the 30-layer rollout, the
 30-layer recache at a prompt switch and the 400-chunk int8 rollout with recache;
 the shader clock read during the timed work) and the CPU oracle timed on this host
 as a baseline.
@@ -18,7 +18,7 @@ as a baseline.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--no-components] [--no-rollouts]
                     [--workload steady|rollout|long_int8|recache|sweep|append|steady_int8|steady_fp8|
-                                steady_mxfp4]
+                                steady_mxfp4|steady_mxfp8]
 """
 
 import argparse
@@ -72,7 +72,7 @@ def _attn_flops(H, D, nq, nk):
 def _append_bytes(rows, D, kv):
     """Algorithmic bytes of writing `rows` (token, head) rows of K and V into slots: the
     bf16 inputs read, the slot codes written (2, 1 or 1/2 bytes per value for bf16,
-    int8 / fp8, mxfp4) and, for the low-bit caches, one 4-byte scale word per row."""
+    int8 / fp8 / mxfp8, mxfp4) and, for the low-bit caches, one 4-byte scale word per row."""
     code = {"bf16": 2 * D, "mxfp4": D // 2}.get(kv, D)
     return 2 * rows * D * 2 + 2 * rows * code + (2 * rows * 4 if kv != "bf16" else 0)
 
@@ -562,7 +562,7 @@ def run_appends(torch, ll, synth, cfg, n=40):
     back to back, then cold appends with the caches flushed in between."""
     i8w = configs_mod().LONG_INT8.window
     out = {}
-    for kv, W in (("bf16", cfg.window), ("int8", i8w), ("fp8", i8w), ("mxfp4", i8w)):
+    for kv, W in (("bf16", cfg.window), ("int8", i8w), ("fp8", i8w), ("mxfp4", i8w), ("mxfp8", i8w)):
         out[f"{kv}_w{W}_back_to_back"] = run_append_batch(torch, ll, synth, cfg, kv, W, n)
         out[f"{kv}_w{W}_cold"] = run_append_cold(torch, ll, synth, cfg, kv, W)
     return out
@@ -702,7 +702,7 @@ def main():
                          "the components")
     ap.add_argument("--workload", default="steady",
                     choices=["steady", "rollout", "long_int8", "recache", "sweep", "append", "steady_int8",
-                             "steady_fp8", "steady_mxfp4"],
+                             "steady_fp8", "steady_mxfp4", "steady_mxfp8"],
                     help="steady (default): the one-chunk step below; the others print their own "
                          "JSON record: 30-layer rollout, 400-chunk int8 rollout with recache, "
                          "30-layer recache, window/sink sweep, appends only (warm and cold), the "
@@ -746,7 +746,7 @@ def main():
             rec = run_recache_stack(torch, ll, synth, configs.RECACHE)
         elif args.workload == "append":
             rec = {"workload": "appends", "rows": run_appends(torch, ll, synth, configs.STEADY)}
-        elif args.workload in ("steady_int8", "steady_fp8", "steady_mxfp4"):
+        elif args.workload in ("steady_int8", "steady_fp8", "steady_mxfp4", "steady_mxfp8"):
             kv = args.workload.split("_")[1]
             w = configs.Workload(**{**configs.STEADY.__dict__, "window": configs.LONG_INT8.window,
                                     "name": f"steady_h12_d128_t1560_s3_w21_{kv}"})
@@ -772,6 +772,7 @@ def main():
         r8 = run_steady(torch, ll, synth, i8, ksteps, 2, kv="int8")
         rf8 = run_steady(torch, ll, synth, i8, ksteps, 2, kv="fp8")
         rm4 = run_steady(torch, ll, synth, i8, ksteps, 2, kv="mxfp4")
+        rm8 = run_steady(torch, ll, synth, i8, ksteps, 2, kv="mxfp8")
         rc = run_recache_layer(torch, ll, synth, configs.RECACHE)
         components = {
             "attention_bf16": _attention_component(r),
@@ -791,6 +792,10 @@ def main():
             "append_mxfp4_w21": _append_component(rm4),
             "append_mxfp4_w21_back_to_back": run_append_batch(torch, ll, synth, cfg, "mxfp4", i8.window),
             "append_mxfp4_w21_cold": run_append_cold(torch, ll, synth, cfg, "mxfp4", i8.window),
+            "attention_mxfp8_w21": _attention_component(rm8),
+            "append_mxfp8_w21": _append_component(rm8),
+            "append_mxfp8_w21_back_to_back": run_append_batch(torch, ll, synth, cfg, "mxfp8", i8.window),
+            "append_mxfp8_w21_cold": run_append_cold(torch, ll, synth, cfg, "mxfp8", i8.window),
             "recache_layer": rc,
         }
         if not args.no_rollouts:

@@ -57,7 +57,7 @@ extern "C" {
 
 typedef struct ll_cache ll_cache; /* opaque; owns its slot memory */
 
-typedef enum { LL_KV_BF16 = 0, LL_KV_INT8 = 1, LL_KV_FP8 = 2, LL_KV_MXFP4 = 3 } ll_kv_dtype;
+typedef enum { LL_KV_BF16 = 0, LL_KV_INT8 = 1, LL_KV_FP8 = 2, LL_KV_MXFP4 = 3, LL_KV_MXFP8 = 4 } ll_kv_dtype;
 
 typedef enum {
   LL_OK = 0,
@@ -100,6 +100,11 @@ typedef enum {
  *                     ties to the even code, with the sign of x (so -0 and negative
  *                     values that round to zero give code 8).  Dequantised values
  *                     value(q) * 2^e are exact bf16 values.
+ *                     LL_KV_MXFP8: OCP MX 8-bit codes (E4M3 as above) with one
+ *                     power-of-two scale 2^e per block of 32 values of a row:
+ *                     e = max(floor(log2 absmax) - 8, -117) (-117 for an all-zero
+ *                     block), q = E4M3(clamp(x / 2^e, -448, 448)) nearest, ties to
+ *                     even, sign kept; value(q) * 2^e is an exact bf16 value.
  *                     [LL2-wmrh §15.2-§15.3]: the history cache kept in low precision
  *                     (4-bit on the page's hardware) and dequantised where it is used.
  *                     Every division above is one IEEE binary32 division.
@@ -107,7 +112,7 @@ typedef enum {
  *
  * Device memory, one allocation made here (no later call allocates):
  * layers * 2 * (S+W) * T * heads * head_dim * (2, 1 or 1/2) bytes of slots, plus
- * layers * 2 * (S+W) * T * heads * 4 bytes of scales for int8 / fp8 / mxfp4, plus per layer
+ * layers * 2 * (S+W) * T * heads * 4 bytes of scales for the low-bit caches, plus per layer
  * an attention work area for split key walks (2 * CUs partial results of 256 rows *
  * (head_dim + 2) * 4 bytes and CUs arrival counters: about 68 MB for head_dim 128 on
  * 256 CUs).  Slot contents start undefined; no slot is visible until written.  The
@@ -178,8 +183,8 @@ ll_status ll_cache_append(ll_cache *c, int layer, const void *K, const void *V,
  * with full visibility inside the own chunk:
  *     out = softmax((Q K^T) / sqrt(head_dim)) V   per head, over those keys.
  * The cache is read only (denoise passes of one chunk may call this repeatedly).
- * For LL_KV_INT8 / LL_KV_FP8 / LL_KV_MXFP4 caches the cached keys/values are
- * dequantised (value(q) * scale); the own chunk is used as given.
+ * For the low-bit caches the cached keys/values are dequantised (value(q) * scale);
+ * the own chunk is used as given.
  *   Q, K_chunk, V_chunk   [n_frames*T][heads][head_dim] bf16 (n_frames >= 1)
  *   out                   [n_frames*T][heads][head_dim] bf16, written completely
  * Arithmetic: bf16 MFMA products, fp32 accumulation and softmax statistics, bf16
@@ -269,8 +274,8 @@ ll_status ll_kv_project(const void *h, const void *W_K, const void *W_V, int n_t
  *   W_K, W_V  [heads*head_dim][d_in] bf16
  *   n_frames  must equal min(f0, S+W) (else LL_ERR_STATE)
  *   d_in      a multiple of 64; heads*head_dim must be a multiple of 128
- * bf16, int8 and fp8 caches; an LL_KV_MXFP4 cache returns LL_ERR_INVALID (use
- * ll_kv_project, then ll_cache_recache).
+ * bf16, int8 and fp8 caches; an LL_KV_MXFP4 or LL_KV_MXFP8 cache returns
+ * LL_ERR_INVALID (use ll_kv_project, then ll_cache_recache).
  * Errors: LL_ERR_INVALID, LL_ERR_STATE, LL_ERR_HIP.
  */
 ll_status ll_cache_recache_from_hidden(ll_cache *c, int layer, const void *h, const void *W_K,
@@ -287,10 +292,11 @@ ll_status ll_cache_frames_seen(const ll_cache *c, int layer, int64_t *f0);
 ll_status ll_cache_slot_frames(const ll_cache *c, int layer, int64_t *frame_of_slot);
 
 /* Device pointers of `layer`'s slot arrays (read them after synchronising):
- *   K, V        [S+Ss+W][T][heads][head_dim], bf16, int8 or E4M3 bytes (kv_dtype);
+ *   K, V        [S+Ss+W][T][heads][head_dim], bf16, int8 or E4M3 bytes (kv_dtype:
+ *               bf16, int8, fp8 or MXFP8);
  *               for LL_KV_MXFP4 [S+Ss+W][T][heads][head_dim/2] bytes, byte k holding
  *               value 2k in its low 4 bits and value 2k+1 in its high 4 bits
- *   K_scale, V_scale  [S+Ss+W][T][heads] fp32 for int8 / fp8 caches; for LL_KV_MXFP4
+ *   K_scale, V_scale  [S+Ss+W][T][heads] fp32 for int8 / fp8 caches; for the MX caches
  *               [S+Ss+W][T][heads] uint32, byte b = e + 127 of the row's block b
  *               (bytes past head_dim/32 are 0); NULL for bf16
  * Any output pointer may be NULL. */

@@ -26,8 +26,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllcache.
 LIB_DEBUG_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllcache_debug.so")
 
 LL_OK, LL_ERR_INVALID, LL_ERR_OOM, LL_ERR_STATE, LL_ERR_HIP = range(5)
-LL_KV_BF16, LL_KV_INT8, LL_KV_FP8, LL_KV_MXFP4 = 0, 1, 2, 3
-_KV_NAMES = {"bf16": LL_KV_BF16, "int8": LL_KV_INT8, "fp8": LL_KV_FP8, "mxfp4": LL_KV_MXFP4}
+LL_KV_BF16, LL_KV_INT8, LL_KV_FP8, LL_KV_MXFP4, LL_KV_MXFP8 = 0, 1, 2, 3, 4
+_KV_NAMES = {"bf16": LL_KV_BF16, "int8": LL_KV_INT8, "fp8": LL_KV_FP8, "mxfp4": LL_KV_MXFP4,
+             "mxfp8": LL_KV_MXFP8}
 MAX_SLOTS = 128
 
 EXPORTS = [
@@ -124,7 +125,7 @@ class Cache:
         self.T, self.S, self.W, self.Ss = tokens_per_frame, sink, window, shot_sink
         self.kv_dtype = kv_dtype
         if kv_dtype not in _KV_NAMES and kv_dtype not in _KV_NAMES.values():
-            raise ValueError(f"kv_dtype must be 'bf16', 'int8', 'fp8' or 'mxfp4', got {kv_dtype!r}")
+            raise ValueError(f"kv_dtype must be one of {sorted(_KV_NAMES)}, got {kv_dtype!r}")
         dt = _KV_NAMES.get(kv_dtype, kv_dtype)
         self.kv_code = dt
         h = ctypes.c_void_p()
@@ -235,9 +236,9 @@ class Cache:
         """Copy the layer's slot arrays to the host (synchronising the device first).
 
         Returns a dict with 'K', 'V' as uint8 byte arrays shaped [S+W][T][H][row bytes]
-        (row bytes: 2 D for bf16, D for int8 / fp8, D/2 for mxfp4) and, for the low-bit
-        caches, 'K_scale', 'V_scale' shaped [S+W][T][H]: float32 for int8 / fp8, uint32
-        words of block-scale bytes for mxfp4.
+        (row bytes: 2 D for bf16, D for int8 / fp8 / mxfp8, D/2 for mxfp4) and, for the
+        low-bit caches, 'K_scale', 'V_scale' shaped [S+W][T][H]: float32 for int8 / fp8,
+        uint32 words of block-scale bytes for mxfp4 / mxfp8.
         """
         import numpy as np
         import torch
@@ -250,7 +251,7 @@ class Cache:
                "V": _d2h(vp, nbytes).reshape(slots, self.T, self.heads, row)}
         if ksp:
             sb = slots * self.T * self.heads * 4
-            sdt = np.uint32 if self.kv_code == LL_KV_MXFP4 else np.float32
+            sdt = np.uint32 if self.kv_code in (LL_KV_MXFP4, LL_KV_MXFP8) else np.float32
             out["K_scale"] = _d2h(ksp, sb).view(sdt).reshape(slots, self.T, self.heads)
             out["V_scale"] = _d2h(vsp, sb).view(sdt).reshape(slots, self.T, self.heads)
         return out

@@ -152,6 +152,8 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int64_t rs, int wave, int la
 //      Q with the codes);
 //   V: the dequantised values q * s rounded to bf16 (LongLive-2.0 explainer, wmrh.cn,
 //      §15.3: dequantised where they are consumed), so the tile's P*V is the bf16 one.
+// MXFP8 codes (E4M3 with a power-of-two scale per 32 values) take the same staging,
+// but K and V both widen exactly to value * 2^e (a bf16 value): an ordinary bf16 tile.
 // No wave reads another wave's staging rows, so no barrier is needed in between.
 template <int D, int NW, int FMT>
 struct QTile {
@@ -198,6 +200,28 @@ struct QTile {
       const u32x4 qk = *reinterpret_cast<const u32x4*>(stage + i * ROWS * D + 16 * lane);
       const u32x4 qv = *reinterpret_cast<const u32x4*>(stage + STAGE + i * ROWS * D + 16 * lane);
       const float* sc = sst + (wave * ITER + it) * 128 + lane / CH8;
+      if constexpr (FMT == kKvMxfp8) {
+        // MXFP8: the lane's 16 codes are half of block c16 / 2; value * 2^e is exact in
+        // bf16 for K and V alike, so both widen to plain bf16 tiles (no per-key factors)
+        const int sh = 8 * (c16 >> 1);
+        const float sk = __builtin_bit_cast(float, ((__builtin_bit_cast(uint32_t, sc[0]) >> sh) & 0xFFu) << 23);
+        const float sv = __builtin_bit_cast(float, ((__builtin_bit_cast(uint32_t, sc[64]) >> sh) & 0xFFu) << 23);
+        auto w8 = [](uint32_t q, float s, bool hi) __attribute__((always_inline)) {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, s, true)
+                              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, s, false);
+          return __builtin_bit_cast(uint32_t, v);
+        };
+        *reinterpret_cast<u32x4*>(lk + r * D + 8 * swz<D>(r, 2 * c16)) =
+            u32x4{w8(qk.x, sk, false), w8(qk.x, sk, true), w8(qk.y, sk, false), w8(qk.y, sk, true)};
+        *reinterpret_cast<u32x4*>(lk + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
+            u32x4{w8(qk.z, sk, false), w8(qk.z, sk, true), w8(qk.w, sk, false), w8(qk.w, sk, true)};
+        *reinterpret_cast<u32x4*>(lv + r * D + 8 * swz<D>(r, 2 * c16)) =
+            u32x4{w8(qv.x, sv, false), w8(qv.x, sv, true), w8(qv.y, sv, false), w8(qv.y, sv, true)};
+        *reinterpret_cast<u32x4*>(lv + r * D + 8 * swz<D>(r, 2 * c16 + 1)) =
+            u32x4{w8(qv.z, sv, false), w8(qv.z, sv, true), w8(qv.w, sv, false), w8(qv.w, sv, true)};
+        continue;
+      }
       const float sk = sc[0], sv = sc[64];
       *reinterpret_cast<u32x4*>(lk + r * D + 8 * swz<D>(r, 2 * c16)) =
           u32x4{code2_to_bf16x2<FMT>(qk.x, 0), code2_to_bf16x2<FMT>(qk.x, 2), code2_to_bf16x2<FMT>(qk.y, 0),
@@ -832,7 +856,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_kernel(const AttnParams p,
   __shared__ __attribute__((aligned(1024))) uint16_t sm_k1[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v0[G::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sm_v1[G::TILE];
-  constexpr bool KV8 = KVQ != kKvBf16;   // quantised cache (int8, fp8 or fp4 codes), staged tiles
+  constexpr bool KV8 = KVQ != kKvBf16;   // quantised cache (int8, fp8, MXFP4 or MXFP8 codes), staged tiles
   constexpr bool KSC = KVQ == kKvInt8 || KVQ == kKvFp8;   // per-row scales: per-key score factors
   using QT = std::conditional_t<KVQ == kKvMxfp4, QTile4<D, NW>, QTile<D, NW, KVQ>>;
   __shared__ __attribute__((aligned(16))) float sm_kf0[KSC ? BN : 1];   // per-key score factors
@@ -1077,6 +1101,7 @@ hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t 
       case kKvInt8: return big ? launch_t<128, 1, 8, kKvInt8>(p, s) : launch_t<128, 1, 4, kKvInt8>(p, s);
       case kKvFp8: return big ? launch_t<128, 1, 8, kKvFp8>(p, s) : launch_t<128, 1, 4, kKvFp8>(p, s);
       case kKvMxfp4: return big ? launch_t<128, 1, 8, kKvMxfp4>(p, s) : launch_t<128, 1, 4, kKvMxfp4>(p, s);
+      case kKvMxfp8: return big ? launch_t<128, 1, 8, kKvMxfp8>(p, s) : launch_t<128, 1, 4, kKvMxfp8>(p, s);
     }
   } else if (D == 64) {
     switch (kv_fmt) {
@@ -1084,6 +1109,7 @@ hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t 
       case kKvInt8: return big ? launch_t<64, 2, 4, kKvInt8>(p, s) : launch_t<64, 1, 4, kKvInt8>(p, s);
       case kKvFp8: return big ? launch_t<64, 2, 4, kKvFp8>(p, s) : launch_t<64, 1, 4, kKvFp8>(p, s);
       case kKvMxfp4: return big ? launch_t<64, 2, 4, kKvMxfp4>(p, s) : launch_t<64, 1, 4, kKvMxfp4>(p, s);
+      case kKvMxfp8: return big ? launch_t<64, 2, 4, kKvMxfp8>(p, s) : launch_t<64, 1, 4, kKvMxfp8>(p, s);
     }
   }
   return hipErrorInvalidValue;

@@ -1,8 +1,9 @@
 // cache.cpp -- the C ABI: cache handle, host bookkeeping, validation, kernel dispatch.
 //
 // The handle owns one device allocation holding, per layer, the K and V slot arrays
-// [S+W][T][H][D] (bf16, int8 or fp8; MXFP4 [S+W][T][H][D/2] bytes), for the low-bit
-// caches their [S+W][T][H] scales (fp32, or for MXFP4 words of E8M0 block-scale bytes),
+// [S+W][T][H][D] (bf16, int8, fp8 or MXFP8; MXFP4 [S+W][T][H][D/2] bytes), for the
+// low-bit caches their [S+W][T][H] scales (fp32, or for the MX formats words of E8M0
+// block-scale bytes),
 // and the attention work area of the split key walk (partials and counters).  Host
 // bookkeeping per layer: frames seen (f0) and the frame held by each slot.  Every
 // argument is checked before the first HIP call so that errors are testable on a
@@ -255,8 +256,10 @@ __global__ void poison_kernel(uint32_t* p, int64_t n_words, uint32_t pattern) {
     p[i] = pattern;
 }
 
-// Scale words of a poisoned slot: fp32 NaN (int8 / fp8), or E8M0 NaN bytes (MXFP4).
-uint32_t scale_poison(int kv_dtype) { return kv_dtype == LL_KV_MXFP4 ? 0xFFFFFFFFu : 0x7FC00000u; }
+// Scale words of a poisoned slot: fp32 NaN (int8 / fp8), or E8M0 NaN bytes (MX formats).
+uint32_t scale_poison(int kv_dtype) {
+  return kv_dtype == LL_KV_MXFP4 || kv_dtype == LL_KV_MXFP8 ? 0xFFFFFFFFu : 0x7FC00000u;
+}
 
 hipError_t poison(void* p, size_t bytes, uint32_t pattern, hipStream_t s) {
   const int64_t words = int64_t(bytes / 4);
@@ -312,12 +315,13 @@ ll_status ll_cache_create_shots(int layers, int heads, int head_dim, int tokens_
   const int64_t slots = int64_t(sink_frames) + shot_sink_frames + window_frames;
   if (slots < 1 || slots > LL_MAX_SLOTS)
     return fail(LL_ERR_INVALID, "sink_frames + shot_sink_frames + window_frames must be in [1, %d]", LL_MAX_SLOTS);
-  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8 && kv_dtype != LL_KV_FP8 && kv_dtype != LL_KV_MXFP4)
+  if (kv_dtype != LL_KV_BF16 && kv_dtype != LL_KV_INT8 && kv_dtype != LL_KV_FP8 && kv_dtype != LL_KV_MXFP4 &&
+      kv_dtype != LL_KV_MXFP8)
     return fail(LL_ERR_INVALID, "unknown kv_dtype %d", kv_dtype);
   const int64_t rows = int64_t(tokens_per_frame) * heads;
   if (slots * tokens_per_frame > kMaxRows || rows > kMaxRows) return fail(LL_ERR_INVALID, "cache too large");
   const bool quantised = kv_dtype != LL_KV_BF16;
-  // code bytes per (token, head) row: 2 per value (bf16), 1 (int8, fp8) or 1/2 (MXFP4)
+  // code bytes per (token, head) row: 2 per value (bf16), 1 (int8, fp8, MXFP8) or 1/2 (MXFP4)
   const int64_t row_bytes = kv_dtype == LL_KV_BF16 ? 2 * head_dim : kv_dtype == LL_KV_MXFP4 ? head_dim / 2 : head_dim;
   auto round256 = [](int64_t b) { return (b + 255) / 256 * 256; };
   const int64_t kv_bytes = round256(slots * rows * row_bytes);
@@ -544,8 +548,8 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
     return fail(LL_ERR_INVALID, "heads*head_dim = %lld must be a multiple of 128", (long long)d_out);
   const int64_t f0 = c->f0[size_t(layer)];
   const int64_t fs = c->fs[size_t(layer)];
-  if (c->kv_dtype == LL_KV_MXFP4)
-    return fail(LL_ERR_INVALID, "recache_from_hidden: MXFP4 caches take ll_kv_project + ll_cache_recache");
+  if (c->kv_dtype == LL_KV_MXFP4 || c->kv_dtype == LL_KV_MXFP8)
+    return fail(LL_ERR_INVALID, "recache_from_hidden: MX caches take ll_kv_project + ll_cache_recache");
   const int64_t need = ll::cached_frames(f0, c->layout(), fs);
   if (need == 0) return fail(LL_ERR_STATE, "recache_from_hidden: layer %d holds no frames", layer);
   if (n_frames != need)

@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, int byte0) {
 }
 
 // Cache code formats (same values as the C ABI's kv_dtype).
-enum KvFmt : int { kKvBf16 = 0, kKvInt8 = 1, kKvFp8 = 2, kKvMxfp4 = 3 };
+enum KvFmt : int { kKvBf16 = 0, kKvInt8 = 1, kKvFp8 = 2, kKvMxfp4 = 3, kKvMxfp8 = 4 };
 
 template <int FMT>
 __device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t w, int byte0) {

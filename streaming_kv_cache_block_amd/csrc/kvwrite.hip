@@ -19,8 +19,8 @@
 // OCP E4M3 value) and the quotient, clamped to [-448, 448] (it exceeds that only when
 // x * 448 overflowed), rounded to E4M3 (nearest, ties to even) by the hardware
 // conversion.  LongLive-2.0 explainer, wmrh.cn, §15.2: the history cache is
-// stored in low precision to save memory and traffic.  MXFP4 caches: see
-// mx4_frames_kernel.
+// stored in low precision to save memory and traffic.  MXFP4 / MXFP8 caches: see
+// mx_frames_kernel.
 #include "device_common.h"
 #include "launch.h"
 
@@ -214,19 +214,25 @@ __global__ __launch_bounds__(kThreads) void quant_frames_kernel(const WriteParam
   }
 }
 
-// MXFP4 caches (OCP MX: E2M1 codes, one E8M0 power-of-two scale per block of 32
-// values; LongLive-2.0 explainer, wmrh.cn, §15.2: the history cache in 4-bit floating
-// point).  Same lane layout as the quantising writes above: D/16 lanes per (token,
-// head) row, 16 consecutive values per lane, so a block of 32 is a lane pair.  Per
-// block: a = max |x| (lane pair, one DPP swap), e = max(floor(log2 a) - 2, -125) read
-// off a's exponent field (a bf16 value; 0 and subnormals give -125), y = x * 2^-e (exact),
-// and the hardware conversion to E2M1 with unit scale: nearest, ties to the even code,
-// saturating at 6, sign kept (checked against the format definition for every
-// midpoint, the saturation range and signed zeros).  A lane's 16 codes (8 bytes, value
-// 2k in the low half of byte k) leave with one 8-byte store; the first lane of a row
-// gathers the row's block exponents into one scale word (byte b = e_b + 127).
-template <int D>
-__global__ __launch_bounds__(kThreads) void mx4_frames_kernel(const WriteParams p) {
+// MX caches (OCP Microscaling: one E8M0 power-of-two scale per block of 32 values;
+// elements E2M1 for MXFP4, E4M3 for MXFP8; LongLive-2.0 explainer, wmrh.cn, §15.2: the
+// history cache in low-precision floating point).  Same lane layout as the quantising
+// writes above: D/16 lanes per (token, head) row, 16 consecutive values per lane, so a
+// block of 32 is a lane pair.  Per block: a = max |x| (lane pair, one DPP swap),
+// e = max(floor(log2 a) - EMAX, EMIN) read off a's exponent field (a bf16 value; 0 and
+// subnormals give EMIN), y = x * 2^-e (exact), and the hardware conversion with unit
+// scale: nearest, ties to the even code, sign kept (E2M1 saturates at 6 by itself;
+// E4M3 values are clamped to +-448 first).  Both conversions were checked against the
+// formats' definitions (midpoints, saturation, signed zeros).  A lane's 16 codes leave
+// with one 8-byte (MXFP4, value 2k in the low half of byte k) or 16-byte (MXFP8) store;
+// the first lane of a row gathers the row's block exponents into one scale word (byte
+// b = e_b + 127).
+template <int D, int FMT>
+__global__ __launch_bounds__(kThreads) void mx_frames_kernel(const WriteParams p) {
+  constexpr bool FP4 = FMT == kKvMxfp4;
+  constexpr int EMAX = FP4 ? 2 : 8;        // exponent of the element format's largest value
+  constexpr int EMIN = FP4 ? -125 : -117;  // smallest value * 2^EMIN is 2^-126, a normal bf16
+  constexpr int RB = FP4 ? D / 2 : D;      // code bytes per row
   constexpr int VPL = kQuantValues;
   constexpr int LPR = D / VPL;
   constexpr int GROUPS = kThreads / LPR;
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void mx4_frames_kernel(const WriteParams 
   const int lane = threadIdx.x & 63;
   const int64_t row0 = (int64_t(blockIdx.x) * GROUPS + threadIdx.x / LPR) * RPG;
   const uint16_t* src = (isv ? p.srcV : p.srcK) + int64_t(p.plan_src[e]) * p.rows_per_frame * D;
-  uint8_t* dst = static_cast<uint8_t*>(isv ? p.dstV : p.dstK) + int64_t(p.plan_slot[e]) * p.rows_per_frame * (D / 2);
+  uint8_t* dst = static_cast<uint8_t*>(isv ? p.dstV : p.dstK) + int64_t(p.plan_slot[e]) * p.rows_per_frame * RB;
   uint32_t* dsc = reinterpret_cast<uint32_t*>(isv ? p.dstVs : p.dstKs) + int64_t(p.plan_slot[e]) * p.rows_per_frame;
 
   u32x4 w[RPG][VPL / 8];
@@ -265,15 +271,26 @@ __global__ __launch_bounds__(kThreads) void mx4_frames_kernel(const WriteParams 
 #pragma unroll
     for (int k = 0; k < VPL; ++k) a = fmaxf(a, fabsf(x[k]));
     a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false)));
-    const int eb = max(int(__builtin_bit_cast(uint32_t, a) >> 23) - 129, -125);
+    const int eb = max(int(__builtin_bit_cast(uint32_t, a) >> 23) - 127 - EMAX, EMIN);
     const float inv = __builtin_bit_cast(float, uint32_t(127 - eb) << 23);   // 2^-e, a normal float
-    uint32_t c[2] = {0u, 0u};
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+    if constexpr (FP4) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h] * inv, x[8 * h + 1] * inv, 1.0f, 0);
-      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 2] * inv, x[8 * h + 3] * inv, 1.0f, 1);
-      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 4] * inv, x[8 * h + 5] * inv, 1.0f, 2);
-      c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 6] * inv, x[8 * h + 7] * inv, 1.0f, 3);
+      for (int h = 0; h < 2; ++h) {
+        c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h] * inv, x[8 * h + 1] * inv, 1.0f, 0);
+        c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 2] * inv, x[8 * h + 3] * inv, 1.0f, 1);
+        c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 4] * inv, x[8 * h + 5] * inv, 1.0f, 2);
+        c[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[h], x[8 * h + 6] * inv, x[8 * h + 7] * inv, 1.0f, 3);
+      }
+    } else {
+      float y[VPL];
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) y[k] = fminf(fmaxf(x[k] * inv, -448.0f), 448.0f);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        c[h] = f32x2_to_e4m3x2(y[4 * h], y[4 * h + 1], 0u, false);
+        c[h] = f32x2_to_e4m3x2(y[4 * h + 2], y[4 * h + 3], c[h], true);
+      }
     }
     // scale word of the row: block b's byte comes from lane sub = 2 b of the row
     const int byte = eb + 127;
@@ -282,8 +299,12 @@ __global__ __launch_bounds__(kThreads) void mx4_frames_kernel(const WriteParams 
     for (int b = 1; b < D / 32; ++b)
       word |= uint32_t(__builtin_amdgcn_ds_bpermute(4 * ((lane + 2 * b) & 63), byte)) << (8 * b);
     if (row < p.rows_per_frame) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_nontemporal_store(u32x2{c[0], c[1]}, reinterpret_cast<u32x2*>(dst + row * (D / 2) + 8 * sub));
+      if constexpr (FP4) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32x2{c[0], c[1]}, reinterpret_cast<u32x2*>(dst + row * RB + 8 * sub));
+      } else {
+        __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, reinterpret_cast<u32x4*>(dst + row * RB + 16 * sub));
+      }
       if (sub == 0) dsc[row] = word;
     }
   }
@@ -302,9 +323,11 @@ hipError_t launch_kv_write(const WriteParams& p, int D, int kv_fmt, hipStream_t 
   }
   const int rows_per_block = kThreads / (D / kQuantValues) * kQuantRows;
   dim3 grid(unsigned((p.rows_per_frame + rows_per_block - 1) / rows_per_block), unsigned(p.n), 2);
-  if (kv_fmt == kKvMxfp4) {
-    if (D == 128) hipLaunchKernelGGL(mx4_frames_kernel<128>, grid, dim3(kThreads), 0, s, p);
-    else if (D == 64) hipLaunchKernelGGL(mx4_frames_kernel<64>, grid, dim3(kThreads), 0, s, p);
+  if (kv_fmt == kKvMxfp4 || kv_fmt == kKvMxfp8) {
+    if (D == 128 && kv_fmt == kKvMxfp4) hipLaunchKernelGGL((mx_frames_kernel<128, kKvMxfp4>), grid, dim3(kThreads), 0, s, p);
+    else if (D == 64 && kv_fmt == kKvMxfp4) hipLaunchKernelGGL((mx_frames_kernel<64, kKvMxfp4>), grid, dim3(kThreads), 0, s, p);
+    else if (D == 128) hipLaunchKernelGGL((mx_frames_kernel<128, kKvMxfp8>), grid, dim3(kThreads), 0, s, p);
+    else if (D == 64) hipLaunchKernelGGL((mx_frames_kernel<64, kKvMxfp8>), grid, dim3(kThreads), 0, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }

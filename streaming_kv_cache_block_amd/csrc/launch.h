@@ -20,8 +20,8 @@ struct AttnParams {
   uint16_t* out;
   const void* cK;       // cached keys: the layer's slot array (bf16, int8, fp8 or fp4 codes)
   const void* cV;
-  const float* cKs;     // int8 / fp8: per (token, head) scales; mxfp4: per (token, head)
-  const float* cVs;     //   words of four E8M0 block-scale bytes (read as raw bits)
+  const float* cKs;     // int8 / fp8: per (token, head) scales; MX formats: per (token,
+  const float* cVs;     //   head) words of four E8M0 block-scale bytes (read as raw bits)
   int nq;               // query rows = own-chunk key rows
   int ncache;           // cached key rows (sum of the runs)
   int nrun;             // runs of cached rows (0..kMaxRuns)
@@ -47,14 +47,14 @@ inline __host__ __device__ int64_t split_slot_floats(int D, int rows) {
 constexpr int kAttnRows = 256;
 
 // kv_fmt: 0 bf16 cache, 1 int8 codes, 2 fp8 (E4M3) codes (+ fp32 scales), 3 MXFP4
-// (E2M1 codes + E8M0 block scales).
+// (E2M1 codes + E8M0 block scales), 4 MXFP8 (E4M3 codes + E8M0 block scales).
 hipError_t launch_attention(const AttnParams& p, int D, int kv_fmt, hipStream_t s);
 
 // Whether launch_attention would split the key walk of p (given a large enough work
 // area): the blocks leave CUs idle and the walk is long enough.
 bool attention_would_split(const AttnParams& p, int D);
 
-// Copy (bf16) or quantise (int8 / fp8 / mxfp4) whole frames of a [frames*T][H][D] bf16 tensor into
+// Copy (bf16) or quantise (int8 / fp8 / mxfp4 / mxfp8) whole frames of a [frames*T][H][D] bf16 tensor into
 // cache slots.  plan_src[i] is the frame index in the source tensor, plan_slot[i] the
 // destination slot, for i < n.
 struct WriteParams {
@@ -62,7 +62,7 @@ struct WriteParams {
   const uint16_t* srcV;
   void* dstK;           // slot array of the layer: [S+W][T][H][D]
   void* dstV;
-  float* dstKs;         // int8 / fp8: [S+W][T][H] fp32; mxfp4: [S+W][T][H] scale words
+  float* dstKs;         // int8 / fp8: [S+W][T][H] fp32; MX formats: [S+W][T][H] scale words
   float* dstVs;
   int64_t rows_per_frame;  // T*H
   int n;

@@ -7,7 +7,7 @@ which frame); what a chunk may see is decided by the oracle alone.
 import numpy as np
 
 import synth
-from oracle import bf16, mxfp4, quant, ring
+from oracle import bf16, mxfp4, mxfp8, quant, ring
 
 # attention acceptance bounds against the fp32 oracle (same bf16-rounded inputs)
 MAX_ABS = 2e-2
@@ -93,8 +93,8 @@ def compare_rounding_bound(gpu_out, ref, ref_absv, what, kv="bf16"):
     normalises by the sum of what it applied: each applied weight is off by at most
     2^-8 relative, twice, so |sum_j (w~_j - w_j) v_j| <= 2^-7 sum_j p_j |v_j|.  A low-bit
     int8 / fp8 cache's values enter P*V dequantised and rounded to bf16 (2^-8
-    relative), which adds 2^-8 sum_j p_j |v_j|; an MXFP4 cache's dequantised values
-    are bf16 values, so it adds nothing.  The output's bf16 rounding adds at most
+    relative), which adds 2^-8 sum_j p_j |v_j|; an MXFP4 / MXFP8 cache's dequantised
+    values are bf16 values, so it adds nothing.  The output's bf16 rounding adds at most
     2^-8 |out|.
     ref_absv is sum_j p_j |v_j| (the oracle run with |V|)."""
     got = bf16.to_f32(gpu_out if isinstance(gpu_out, np.ndarray) else synth.to_bits(gpu_out)).astype(np.float64)
@@ -102,7 +102,7 @@ def compare_rounding_bound(gpu_out, ref, ref_absv, what, kv="bf16"):
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got - ref)
-    coef = 2.0 ** -7 + (2.0 ** -8 if kv in ("int8", "fp8") else 0.0)   # mxfp4: exact bf16 values
+    coef = 2.0 ** -7 + (2.0 ** -8 if kv in ("int8", "fp8") else 0.0)   # MX formats: exact bf16 values
     bound = coef * ref_absv.astype(np.float64) + 2.0 ** -8 * np.abs(ref) + 1e-6
     worst = np.unravel_index(int(np.argmax(err - bound)), err.shape)
     assert (err <= bound).all(), (f"{what}: err {err[worst]:.3g} > bound {bound[worst]:.3g} at {worst} "
@@ -117,7 +117,7 @@ def abs_bits(bits):
 
 class AbsHistory:
     """history(f) with |V| in place of V: the oracle then returns sum_j p_j |v_j|.  For
-    int8 / fp8 / MXFP4 caches this is also the dequantised |V|, because the rules are
+    int8 / fp8 / MX caches this is also the dequantised |V|, because the rules are
     symmetric (a row or block and its absolute value share the absmax, and rounding to
     the nearest code commutes with the sign)."""
 
@@ -131,7 +131,7 @@ class AbsHistory:
 
 def check_slots(cache, layer, hist, kv_int8=False, kv=None):
     """Slot->frame map equals the slot model; every occupied slot holds exactly the
-    bytes (or the int8 / fp8 / MXFP4 quantisation) of the frame it claims; the occupied
+    bytes (or the int8 / fp8 / MXFP4 / MXFP8 quantisation) of the frame it claims; the occupied
     frames are the cached part of the visible set."""
     if kv is None:
         kv = "int8" if kv_int8 else "bf16"
@@ -148,12 +148,16 @@ def check_slots(cache, layer, hist, kv_int8=False, kv=None):
             assert np.array_equal(got["V"][s].view(np.uint16), vb), f"V slot {s} frame {f}"
         else:
             for name, src in (("K", kb), ("V", vb)):
-                if kv == "mxfp4":
-                    codes, e = mxfp4.quantize(bf16.to_f32(src))
-                    same = got[name][s] == mxfp4.pack_codes(codes)
+                if kv in ("mxfp4", "mxfp8"):
+                    if kv == "mxfp4":
+                        codes, e = mxfp4.quantize(bf16.to_f32(src))
+                        codes = mxfp4.pack_codes(codes)
+                    else:
+                        codes, e = mxfp8.quantize(bf16.to_f32(src))
+                    same = got[name][s] == codes
                     if not same.all():
                         bad = np.argwhere(~same)[:4].tolist()
-                        raise AssertionError(f"{name} fp4 codes slot {s} frame {f}: {int((~same).sum())} bytes "
+                        raise AssertionError(f"{name} {kv} codes slot {s} frame {f}: {int((~same).sum())} bytes "
                                              f"differ, e.g. {bad}")
                     assert np.array_equal(got[name + "_scale"][s], mxfp4.pack_scales(e)), \
                         f"{name} block scales slot {s} frame {f}"

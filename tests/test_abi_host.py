@@ -57,7 +57,7 @@ def test_create_rejects_invalid_arguments_before_touching_hip(L):
         (1, 12, 128, 1560, -1, 12, 0),     # negative sink
         (1, 12, 128, 1560, 0, 0, 0),       # no slots
         (1, 12, 128, 1560, 64, 65, 0),     # too many slots
-        (1, 12, 128, 1560, 3, 12, 4),      # dtype (0 bf16, 1 int8, 2 fp8, 3 mxfp4)
+        (1, 12, 128, 1560, 3, 12, 5),      # dtype (0 bf16, 1 int8, 2 fp8, 3 mxfp4, 4 mxfp8)
         (1, 12, 128, 1560, 3, 12, -1),     # dtype
         (1, 1 << 20, 128, 1 << 20, 3, 12, 0),  # too large
     ]

@@ -76,7 +76,7 @@ def test_cpu_baseline_small_workload():
 def test_append_bytes_count_scales_for_low_bit_caches():
     rows = 3 * 1560 * 12
     assert bench._append_bytes(rows, 128, "bf16") == 4 * rows * 128 * 2
-    for kv in ("int8", "fp8"):   # codes plus one fp32 scale per (token, head) row, K and V
+    for kv in ("int8", "fp8", "mxfp8"):   # one code byte per value plus one 4-byte scale word per row, K and V
         assert bench._append_bytes(rows, 128, kv) == 2 * rows * 128 * 2 + 2 * rows * 128 + 2 * rows * 4
     # mxfp4: half a byte per value plus one word of four block-scale bytes per row
     assert bench._append_bytes(rows, 128, "mxfp4") == 2 * rows * 128 * 2 + 2 * rows * 64 + 2 * rows * 4

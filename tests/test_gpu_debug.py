@@ -1,7 +1,7 @@
 """The debug library (host side built with LL_DEBUG) on the GPU.
 
 Every slot of a fresh debug cache is poisoned (bf16 NaN, NaN scales for int8 / fp8,
-E8M0 NaN block-scale bytes 0xFF for MXFP4)
+E8M0 NaN block-scale bytes 0xFF for MXFP4 / MXFP8)
 and the slots a recache rewrites are poisoned again just before.  So:
   * a toy rollout through the debug library gives finite outputs, byte for byte the
     normal library's: attention never read a slot no frame was written to;
@@ -39,7 +39,7 @@ def _poisoned(got, kv):
     if kv == "bf16":
         k = np.isnan(bf16.to_f32(got["K"].view(np.uint16))).reshape(got["K"].shape[0], -1).any(axis=1)
         v = np.isnan(bf16.to_f32(got["V"].view(np.uint16))).reshape(got["V"].shape[0], -1).any(axis=1)
-    elif kv == "mxfp4":   # a written block scale byte is e + 127 <= 252; 0xFF is E8M0's NaN
+    elif kv in ("mxfp4", "mxfp8"):   # a written block scale byte is e + 127 <= 252; 0xFF is E8M0's NaN
         k = (got["K_scale"].view(np.uint8) == 0xFF).reshape(got["K_scale"].shape[0], -1).any(axis=1)
         v = (got["V_scale"].view(np.uint8) == 0xFF).reshape(got["V_scale"].shape[0], -1).any(axis=1)
     else:
@@ -48,7 +48,7 @@ def _poisoned(got, kv):
     return k | v
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 def test_debug_library_poisons_and_matches(torch_gpu, kv):
     cfg = configs.TOY
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
@@ -86,7 +86,7 @@ def test_debug_library_poisons_and_matches(torch_gpu, kv):
     hist.recache_window(K_w, V_w)
     assert not _poisoned(dbg.slot_bytes(0), kv).any()
     check_slots(dbg, 0, hist, kv=kv)
-    if kv == "mxfp4":   # no fused projection epilogue for this format
+    if kv in ("mxfp4", "mxfp8"):   # no fused projection epilogue for the MX formats
         dbg.close()
         ref.close()
         return

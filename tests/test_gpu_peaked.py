@@ -99,7 +99,7 @@ def _check_all_rows(torch, cache, hist, kv, W, q, kc, vc, what, scale_gate):
     assert np.array_equal(synth.to_bits(again), synth.to_bits(out)), what
 
 
-@pytest.mark.parametrize("kv,W", [("bf16", 12), ("int8", 21), ("fp8", 21), ("mxfp4", 21)])
+@pytest.mark.parametrize("kv,W", [("bf16", 12), ("int8", 21), ("fp8", 21), ("mxfp4", 21), ("mxfp8", 21)])
 def test_full_shape_peaked_scores_all_rows(torch_gpu, kv, W):
     sigma = 3.0
     gen = lambda layer, k: (synth.normal_bf16(SHAPE, sigma, 700, W, 1, k),
@@ -110,7 +110,7 @@ def test_full_shape_peaked_scores_all_rows(torch_gpu, kv, W):
     cache.close()
 
 
-@pytest.mark.parametrize("kv,W", [("bf16", 12), ("int8", 21), ("fp8", 21), ("mxfp4", 21)])
+@pytest.mark.parametrize("kv,W", [("bf16", 12), ("int8", 21), ("fp8", 21), ("mxfp4", 21), ("mxfp8", 21)])
 def test_full_shape_tail_heavy_scores_through_the_merge(torch_gpu, kv, W):
     gen = lambda layer, k: _tail_heavy(710 + k, [0.0] * C)[1:]
     cache, (hist,) = _prefill(kv, W, gen)

@@ -119,12 +119,13 @@ def test_shot_rollout_with_recache(torch_gpu, kv, S, Ss, W, T, D):
              recache_at=(5, 9), fused_recache_at=(7, 12))
 
 
+@pytest.mark.parametrize("kv", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("S,Ss,W,T,D", [(3, 3, 6, 16, 64), (1, 4, 5, 33, 128)])
-def test_shot_rollout_with_recache_mxfp4(torch_gpu, S, Ss, W, T, D):
-    """As above for an MXFP4 cache, whose recaches all go through ll_cache_recache (the
+def test_shot_rollout_with_recache_mx(torch_gpu, kv, S, Ss, W, T, D):
+    """As above for the MX caches, whose recaches all go through ll_cache_recache (the
     fused projection epilogue takes bf16, int8 and fp8 caches only)."""
-    _log(f"shots kv=mxfp4 S={S} Ss={Ss} W={W} T={T} D={D}")
-    _rollout(torch_gpu, S, Ss, W, T, 2, D, "mxfp4", seed=760 + S * 10 + Ss, recache_at=(5, 7, 9, 12))
+    _log(f"shots kv={kv} S={S} Ss={Ss} W={W} T={T} D={D}")
+    _rollout(torch_gpu, S, Ss, W, T, 2, D, kv, seed=760 + S * 10 + Ss, recache_at=(5, 7, 9, 12))
 
 
 def test_shot_rollout_full_shape(torch_gpu):

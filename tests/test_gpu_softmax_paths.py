@@ -59,7 +59,7 @@ def _staircase(f0, n_frames, T, H, D, seed):
     return tuple(synth.f32_to_bf16_bits(x) for x in (q, k, v))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_staircase_scores(torch_gpu, D, kv):
     T, H, S, W, C = 128, 2, 1, 4, 2
@@ -77,7 +77,7 @@ def test_staircase_scores(torch_gpu, D, kv):
     check_slots(cache, 0, hist, kv=kv)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_wide_score_spread(torch_gpu, D, kv):
     T, H, S, W, C = 96, 2, 2, 5, 3

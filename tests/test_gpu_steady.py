@@ -42,7 +42,7 @@ def _prefill(cache, hist, cfg, layer, n_chunks, tag):
         hist.append(kb, vb)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 def test_steady_state_step(torch_gpu, kv):
     cfg = configs.STEADY
     if kv != "bf16":   # the low-bit workload's window

@@ -68,6 +68,10 @@ def test_toy_rollout_mxfp4(torch_gpu):
     _rollout(torch_gpu, configs.TOY, kv="mxfp4")
 
 
+def test_toy_rollout_mxfp8(torch_gpu):
+    _rollout(torch_gpu, configs.TOY, kv="mxfp8")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("S,W,n_list", [
     (3, 6, [3] * 12),
@@ -124,7 +128,7 @@ def test_append_longer_than_window_and_sink_only(torch_gpu):
             compare_attention(out, ref, f"S={S} W={W} step {j}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 def test_recache_overwrites_every_slot(torch_gpu, kv):
     """Prefill with NaN K/V, recache with finite tensors: no stale (NaN) slot may
     survive, the bytes must be exactly the recache blocks, and attention must match
@@ -165,7 +169,7 @@ def test_recache_overwrites_every_slot(torch_gpu, kv):
     assert e.value.status == ll.LL_ERR_STATE
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 def test_recache_window_keeps_sink(torch_gpu, kv):
     """Window-only recache (techwalker.com article, §六): the window frames' slots get the
     new blocks (oracle.ring's window order), the sink keeps its bytes, and the next
@@ -258,7 +262,7 @@ def test_quantisation_edge_rows_bit_exact(torch_gpu, kv):
         check_slots(cache, 0, hist, kv=kv)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 def test_maximum_slot_count(torch_gpu, kv):
     """S + W = 128 slots (the largest cache the library accepts): sink 8, window 120,
     16 tokens per frame, 2 heads x 128.  50 chunks of 3 frames wrap the 120-slot ring
