@@ -17,9 +17,9 @@
 //     one barrier per tile.  16-byte chunks are XOR-swizzled per row so that the
 //     MFMA operand reads below are free of bank conflicts.  bf16 tiles are copied
 //     global -> LDS by the buffer load-to-LDS path (no registers), one tile ahead;
-//     int8 / fp8 cache tiles are copied as codes (with their scales) into a staging
-//     area the same way, two tiles ahead, and each wave widens the rows it copied to
-//     bf16 while the score MFMAs of the tile before run.
+//     low-bit cache tiles (int8, fp8, MXFP4, MXFP8) are copied as codes (with their
+//     scales) into a staging area the same way, two tiles ahead, and each wave widens
+//     the rows it copied to bf16 while the score MFMAs of the tile before run.
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA: a
 //     lane then holds one query's scores for 16 keys of each 32-key block, so the
 //     running row max needs one register exchange with lane ^ 32
@@ -39,6 +39,9 @@
 //     (exact in bf16) and the per-key factor K scale x log2(e)/sqrt(D) scales the score
 //     column in fp32; V is dequantised to bf16 (q * s, one rounding) when widened.
 //     Both then take the same speculative softmax as bf16 tiles.
+//   * MXFP4 / MXFP8 caches (OCP MX codes with a power-of-two scale per 32 values): K
+//     and V widen exactly to value * 2^e with the hardware's scaled conversions, so
+//     their tiles are ordinary bf16 tiles (no per-key factors).
 //   * Workgroups are numbered so that the query tiles of one head run on the same
 //     XCD (consecutive workgroup ids are dealt round-robin to the 8 XCDs) and share
 //     its L2 while they stream the same keys.
@@ -284,12 +287,23 @@ struct QTile4 {
   // Called by the same wave once its copies of the tile have landed.
   __device__ static void widen(const int8_t* stage, const float* sst, uint16_t* lk, uint16_t* lv, float*, float,
                                int wave, int lane) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int i = wave + it * NW;
       const bool isv = i >= COPIES;
-      const int rl = lane / CH4, blk = lane % CH4;
+      // Lane -> (row, block).  head_dim 128: lane 16 t + 4 u + j takes block j of row
+      // u + 4 ((u + t) & 3), so each 16-lane group reads 16 distinct 16-byte slots of the
+      // staged rows and, for every store k, writes 16 distinct swizzled chunks (the plain
+      // row-major order puts 4 rows x 4 blocks of a group on 4 chunks: 4-way conflicts).
+      int rl, blk;
+      if constexpr (D == 128) {
+        const int u = (lane >> 2) & 3;
+        rl = u + 4 * ((u + (lane >> 4)) & 3);
+        blk = lane & 3;
+      } else {
+        rl = lane / CH4;
+        blk = lane % CH4;
+      }
       const int r = (i % COPIES) * ROWS + rl;
       const u32x4 q = *reinterpret_cast<const u32x4*>(stage + (isv ? STAGE : 0) + r * RB + 16 * blk);
       const uint32_t word = __builtin_bit_cast(uint32_t, sst[i * 64 + rl]);
