@@ -198,11 +198,21 @@ struct QTile {
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int i = wave + it * NW;
-      const int r = i * ROWS + lane / CH8;
-      const int c16 = lane % CH8;
-      const u32x4 qk = *reinterpret_cast<const u32x4*>(stage + i * ROWS * D + 16 * lane);
-      const u32x4 qv = *reinterpret_cast<const u32x4*>(stage + STAGE + i * ROWS * D + 16 * lane);
-      const float* sc = sst + (wave * ITER + it) * 128 + lane / CH8;
+      // Lane -> (row of the copy, 16-byte chunk).  Row-major for int8 / fp8.  MXFP8 with
+      // head_dim 128: the 16-lane group g takes rows g and g + 5 - 2 (g & 1) (0/5, 1/4, 2/7,
+      // 3/6), whose swizzles put the two rows' stores on opposite chunk parities, so each
+      // group's staged reads and its swizzled 16-byte stores hit distinct banks (row-major,
+      // two neighbouring rows share the chunks of each store: 2-way conflicts).
+      int rl = lane / CH8, c16 = lane % CH8;
+      if constexpr (FMT == kKvMxfp8 && D == 128) {
+        const int g = lane >> 4;
+        rl = g + ((lane >> 3) & 1) * (5 - 2 * (g & 1));
+        c16 = lane & 7;
+      }
+      const int r = i * ROWS + rl;
+      const u32x4 qk = *reinterpret_cast<const u32x4*>(stage + (i * ROWS + rl) * D + 16 * c16);
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(stage + STAGE + (i * ROWS + rl) * D + 16 * c16);
+      const float* sc = sst + (wave * ITER + it) * 128 + rl;
       if constexpr (FMT == kKvMxfp8) {
         // MXFP8: the lane's 16 codes are half of block c16 / 2; value * 2^e is exact in
         // bf16 for K and V alike, so both widen to plain bf16 tiles (no per-key factors)
