@@ -264,7 +264,7 @@ ll_status ll_kv_project(const void *h, const void *W_K, const void *W_V, int n_t
 /*
  * ll_cache_recache_from_hidden -- recache straight from hidden states: the
  * projection of ll_kv_project with its results written into the retained slots
- * (and, for int8 / fp8 caches, quantised on the way) instead of into K_all/V_all.
+ * (and, for the low-bit caches, quantised on the way) instead of into K_all/V_all.
  * [LL-dpshk §三 items 4 and 5]: the retained latents' K and V are recomputed from
  * the hidden state under the new prompt and replace the old cache.  The cache
  * bytes equal those of ll_kv_project followed by ll_cache_recache bit for bit;
@@ -274,8 +274,7 @@ ll_status ll_kv_project(const void *h, const void *W_K, const void *W_V, int n_t
  *   W_K, W_V  [heads*head_dim][d_in] bf16
  *   n_frames  must equal min(f0, S+W) (else LL_ERR_STATE)
  *   d_in      a multiple of 64; heads*head_dim must be a multiple of 128
- * bf16, int8 and fp8 caches; an LL_KV_MXFP4 or LL_KV_MXFP8 cache returns
- * LL_ERR_INVALID (use ll_kv_project, then ll_cache_recache).
+ * Every cache format (the low-bit ones quantised by the same rule as append).
  * Errors: LL_ERR_INVALID, LL_ERR_STATE, LL_ERR_HIP.
  */
 ll_status ll_cache_recache_from_hidden(ll_cache *c, int layer, const void *h, const void *W_K,

@@ -548,8 +548,6 @@ ll_status ll_cache_recache_from_hidden(ll_cache* c, int layer, const void* h, co
     return fail(LL_ERR_INVALID, "heads*head_dim = %lld must be a multiple of 128", (long long)d_out);
   const int64_t f0 = c->f0[size_t(layer)];
   const int64_t fs = c->fs[size_t(layer)];
-  if (c->kv_dtype == LL_KV_MXFP4 || c->kv_dtype == LL_KV_MXFP8)
-    return fail(LL_ERR_INVALID, "recache_from_hidden: MX caches take ll_kv_project + ll_cache_recache");
   const int64_t need = ll::cached_frames(f0, c->layout(), fs);
   if (need == 0) return fail(LL_ERR_STATE, "recache_from_hidden: layer %d holds no frames", layer);
   if (n_frames != need)

@@ -90,7 +90,8 @@ __device__ __forceinline__ int64_t slot_row(int m, int T, const int* plan) {
   return s < 0 ? -1 : int64_t(s) * T + m % T;
 }
 
-// Epilogue of the fused recache: bf16 results, or their int8 / fp8 quantisation
+// Epilogue of the fused recache: bf16 results, their MX quantisation (below), or their
+// int8 / fp8 quantisation
 //   a = max |x| over the (token, head) row, scale = a / M,
 //   q = clamp(rint((x * M) / a), -M, M) with M = 127   (0 for an all-zero row),
 //   or the E4M3 rounding of clamp((x * M) / a, -M, M) with M = 448,
@@ -132,6 +133,77 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
           *reinterpret_cast<u32x2*>(dst + 32 * a + 8 * i + 4 * g) = w;
           if (r2 >= 0) *reinterpret_cast<u32x2*>(dst2 + 32 * a + 8 * i + 4 * g) = w;
         }
+    }
+  } else if constexpr (EPI >= 4) {
+    // MX caches (4: MXFP4, E2M1 codes; 5: MXFP8, E4M3 codes), one power-of-two scale per
+    // block of 32 values, the rule of the MX cache writer: a block is half a wave's 64
+    // outputs (32 a ..), held by the lane pair (g = 0, 1) of a token, so its absmax takes
+    // one exchange; e = max(floor(log2 a) - EMAX, EMIN) from the bf16 absmax's exponent
+    // field, y = x * 2^-e (exact), the hardware conversion with unit scale (E4M3 values
+    // clamped to +-448 first).  A wave's 64 outputs are one head (D = 64, blocks 0, 1) or
+    // half of one (D = 128, blocks 0, 1 or 2, 3): its two scale bytes go out in one store.
+    constexpr bool FP4 = EPI == 4;
+    constexpr int EMAX = FP4 ? 2 : 8;
+    constexpr int EMIN = FP4 ? -125 : -117;
+    float x[MB][2][16];
+    int eb[MB][2];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          x[b][a][v] = __builtin_bit_cast(float, pack_bf16x2(acc[a][b][v], 0.0f) << 16);
+          mx = fmaxf(mx, fabsf(x[b][a][v]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        eb[b][a] = max(int(__builtin_bit_cast(uint32_t, mx) >> 23) - 127 - EMAX, EMIN);
+      }
+    uint8_t* base = static_cast<uint8_t*>(z ? pc.slotV : pc.slotK);
+    uint8_t* scb = reinterpret_cast<uint8_t*>(z ? pc.scV : pc.scK);
+    const int head = (n0 + 64 * wn) / pc.D;
+    const int blk0 = ((n0 + 64 * wn) % pc.D) / 32;   // the head's block of half a = 0
+    const int64_t rb = FP4 ? N / 2 : N;              // code bytes per token row
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int row = m0 + WM * wm + 32 * b + r32;
+      if (row >= p.M) continue;
+      const int64_t srow = slot_row(row, pc.T, plan);
+      const int64_t srow2 = slot_row(row, pc.T, plan2);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const float inv = __builtin_bit_cast(float, uint32_t(127 - eb[b][a]) << 23);   // 2^-e
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* xv = &x[b][a][4 * i];
+          const int n_out = n0 + 64 * wn + 32 * a + 8 * i + 4 * g;
+          if constexpr (FP4) {
+            uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xv[0] * inv, xv[1] * inv, 1.0f, 0);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, xv[2] * inv, xv[3] * inv, 1.0f, 1);
+            *reinterpret_cast<uint16_t*>(base + srow * rb + n_out / 2) = uint16_t(c);
+            if (srow2 >= 0) *reinterpret_cast<uint16_t*>(base + srow2 * rb + n_out / 2) = uint16_t(c);
+          } else {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(xv[j] * inv, -448.0f), 448.0f);
+            uint32_t c = f32x2_to_e4m3x2(y[0], y[1], 0u, false);
+            c = f32x2_to_e4m3x2(y[2], y[3], c, true);
+            *reinterpret_cast<uint32_t*>(base + srow * rb + n_out) = c;
+            if (srow2 >= 0) *reinterpret_cast<uint32_t*>(base + srow2 * rb + n_out) = c;
+          }
+        }
+      }
+      if (g == 0) {
+        const uint32_t two = uint32_t(eb[b][0] + 127) | (uint32_t(eb[b][1] + 127) << 8);
+        for (int k = 0; k < 2; ++k) {
+          const int64_t sr = k ? srow2 : srow;
+          if (sr < 0) continue;
+          uint8_t* w = scb + (sr * pc.H + head) * 4;
+          if (pc.D == 64) *reinterpret_cast<uint32_t*>(w) = two;   // bytes 2, 3 stay 0
+          else *reinterpret_cast<uint16_t*>(w + blk0) = uint16_t(two);
+        }
+      }
     }
   } else {
     // bf16-round, then the absmax of each (token, head) row: 32 values per lane, lanes
@@ -238,7 +310,7 @@ __device__ __forceinline__ void cache_epilogue(const ProjToCacheParams& pc, cons
 }
 
 // EPI 0: plain [M][N] outputs; 1: bf16 rows into cache slots; 2: int8 rows + scales;
-// 3: fp8 (E4M3) rows + scales.
+// 3: fp8 (E4M3) rows + scales; 4: MXFP4 rows + block scales; 5: MXFP8 rows + block scales.
 template <int EPI, class SH>
 __global__ __launch_bounds__(SH::NT, SH::MINB) void proj_kernel(const ProjToCacheParams pc, int n_mt, int n_units) {
   constexpr int TM = SH::TM, TN = SH::TN, TK = SH::TK;
@@ -383,6 +455,8 @@ hipError_t launch_kv_project_to_cache(const ProjToCacheParams& p, hipStream_t s)
     case kKvBf16: return launch_proj<1>(p, s);
     case kKvInt8: return launch_proj<2>(p, s);
     case kKvFp8: return launch_proj<3>(p, s);
+    case kKvMxfp4: return launch_proj<4>(p, s);
+    case kKvMxfp8: return launch_proj<5>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,7 +1,8 @@
 """GPU parity of the fused recache (projection whose epilogue writes the cache slots).
 
 ll_cache_recache_from_hidden must leave exactly the bytes that ll_kv_project
-followed by ll_cache_recache leaves (bf16 slots, or int8 / fp8 codes and fp32 scales),
+followed by ll_cache_recache leaves (bf16 slots, int8 / fp8 codes and fp32 scales, or
+MXFP4 / MXFP8 codes and block-scale words),
 and those bytes must match the oracle's cache model fed the projected K/V.
 Shapes: ragged token counts (T not a multiple of the 192- or 256-token tile), head_dim
 64 (two heads per 128-output tile) and 128, output counts that take the 256-wide tiles
@@ -79,7 +80,7 @@ def _case(torch, H, D, T, S, W, d_in, kv, appends, seed):
     return b, hist
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("H,D,T,S,W,d_in,appends", [
     (2, 64, 33, 3, 6, 128, [3, 3]),            # not full: 6 of 9 slots, ragged tiles
     (2, 64, 33, 3, 6, 192, [3, 3, 3, 3, 3]),   # wrapped ring
@@ -96,7 +97,7 @@ def test_fused_recache_matches_project_then_recache(torch_gpu, kv, H, D, T, S, W
     _case(torch_gpu, H, D, T, S, W, d_in, kv, appends, seed=300 + H * 7 + T)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 def test_fused_recache_full_size(torch_gpu, kv):
     cfg = configs.RECACHE
     _case(torch_gpu, cfg.heads, cfg.head_dim, cfg.tokens_per_frame, cfg.sink, cfg.window, cfg.hidden, kv,

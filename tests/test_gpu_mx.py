@@ -1,10 +1,10 @@
 """GPU checks particular to the MX caches (MXFP4: E2M1 codes, MXFP8: E4M3 codes, each
 with one power-of-two scale per block of 32 values): the quantising write on rows built
 to hit every case of the rule, bit for bit against the oracle; attention bit-identical
-to a bf16 cache's on exactly quantisable rows; and the fused projection's refusal of
-these formats.  The MX caches also run through the shared parity tests (toy rollout,
-recache, window recache, maximum slot count, steady step, peaked and tail-heavy full
-shapes, softmax paths, shot sinks, the debug library)."""
+to a bf16 cache's on exactly quantisable rows.  The MX caches also run through the
+shared parity tests (toy rollout, recache, window recache, fused recache, maximum slot
+count, steady step, peaked and tail-heavy full shapes, softmax paths, shot sinks, the
+debug library)."""
 
 import time
 
@@ -15,7 +15,7 @@ import streaming_kv_cache_block_amd as ll
 import synth
 from oracle import attention, bf16, quant
 
-from helpers import History, check_slots, compare_attention
+from helpers import History, check_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -123,28 +123,6 @@ def test_mx_quantisation_edge_rows_bit_exact(torch_gpu, D, huge, kv):
     err = np.abs(got - ref.astype(np.float64))
     assert err.max() <= 2.0 ** -7 * np.abs(ref).max(), (err.max(), np.abs(ref).max())
     _log(f"{kv} edge rows D={D} huge=2^{huge}: codes and scales bit-exact; attention max err {err.max():.3g}")
-
-
-@pytest.mark.parametrize("kv", ["mxfp4", "mxfp8"])
-def test_mx_fused_recache_is_refused(torch_gpu, kv):
-    T, H, D, S, W, C = 16, 2, 64, 3, 6, 3
-    cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
-    kb = synth.normal_bf16((C * T, H, D), 1.0, 33, 0)
-    cache.append(0, synth.to_device(kb), synth.to_device(kb))
-    d_in = 128
-    h = synth.to_device(synth.normal_bf16((C * T, d_in), 1.0, 33, 1))
-    w = synth.to_device(synth.normal_bf16((H * D, d_in), 0.1, 33, 2))
-    with pytest.raises(ll.LLError) as e:
-        cache.recache_from_hidden(0, h, w, w)
-    assert e.value.status == ll.LL_ERR_INVALID
-    # the cache is untouched and still usable
-    hist = History(S, W, T)
-    hist.append(kb, kb)
-    check_slots(cache, 0, hist, kv=kv)
-    q = synth.normal_bf16((C * T, H, D), 1.0, 33, 3)
-    out = cache.attn(0, synth.to_device(q), synth.to_device(kb), synth.to_device(kb))
-    ref = attention.chunk_attention(q, kb, kb, hist, hist.f0, S, W, T, kv=kv)
-    compare_attention(out, ref, f"{kv} after a refused fused recache")
 
 
 @pytest.mark.parametrize("kv", ["mxfp4", "mxfp8"])

@@ -111,21 +111,12 @@ def _rollout(torch, S, Ss, W, T, H, D, kv, seed, recache_at=(), fused_recache_at
         step += 1
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "mxfp4", "mxfp8"])
 @pytest.mark.parametrize("S,Ss,W,T,D", [(3, 3, 6, 16, 64), (1, 4, 5, 33, 128), (0, 2, 3, 24, 64)])
 def test_shot_rollout_with_recache(torch_gpu, kv, S, Ss, W, T, D):
     _log(f"shots kv={kv} S={S} Ss={Ss} W={W} T={T} D={D}")
     _rollout(torch_gpu, S, Ss, W, T, 2, D, kv, seed=700 + S * 10 + Ss,
              recache_at=(5, 9), fused_recache_at=(7, 12))
-
-
-@pytest.mark.parametrize("kv", ["mxfp4", "mxfp8"])
-@pytest.mark.parametrize("S,Ss,W,T,D", [(3, 3, 6, 16, 64), (1, 4, 5, 33, 128)])
-def test_shot_rollout_with_recache_mx(torch_gpu, kv, S, Ss, W, T, D):
-    """As above for the MX caches, whose recaches all go through ll_cache_recache (the
-    fused projection epilogue takes bf16, int8 and fp8 caches only)."""
-    _log(f"shots kv={kv} S={S} Ss={Ss} W={W} T={T} D={D}")
-    _rollout(torch_gpu, S, Ss, W, T, 2, D, kv, seed=760 + S * 10 + Ss, recache_at=(5, 7, 9, 12))
 
 
 def test_shot_rollout_full_shape(torch_gpu):
