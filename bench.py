@@ -383,14 +383,14 @@ def run_append_cold(torch, ll, synth, cfg, kv="bf16", window=None, n=20):
 
 
 def run_recache_layer(torch, ll, synth, cfg, reps=10):
-    """Recache of one layer at the recache workload's size, bf16, int8 and fp8 caches:
+    """Recache of one layer at the recache workload's size, every cache format:
     projection GEMM then rewrite (two launches, K/V round trip through HBM), and the
     fused projection whose epilogue writes the slots; per-launch medians / p10 / p90."""
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     hid = cfg.hidden
     shape = (cfg.nq, H, D)
     res = {}
-    for kv in ("bf16", "int8", "fp8"):
+    for kv in ("bf16", "int8", "fp8", "mxfp4", "mxfp8"):
         cache = ll.Cache(1, H, D, T, S, W, kv_dtype=kv)
         for k in range(cfg.prefill_chunks):
             cache.append(0, synth.normal_bf16_device(shape, 1.0, cfg.seed, 1, k),
