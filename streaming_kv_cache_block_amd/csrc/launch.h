@@ -86,16 +86,16 @@ struct ProjParams {
 hipError_t launch_kv_project(const ProjParams& p, hipStream_t s);
 
 // Projection whose epilogue writes straight into cache slots: output row m (frame
-// m / T, token m % T) goes to slot plan_slot[m / T]; N = H * D.  int8 / fp8 caches get
-// the per-(token, head) quantisation of the bf16-rounded results (same bits as
+// m / T, token m % T) goes to slot plan_slot[m / T]; N = H * D.  Low-bit caches get the
+// quantisation of the bf16-rounded results by their format's rule (same bits as
 // projecting, then quantising the stored bf16 tensor).
 struct ProjToCacheParams {
   ProjParams proj;      // outK/outV unused
   int T, H, D;
-  int kv_fmt;           // 0 bf16, 1 int8, 2 fp8
+  int kv_fmt;           // 0 bf16, 1 int8, 2 fp8, 3 mxfp4, 4 mxfp8
   void* slotK;          // layer slot arrays [S+W][T][H][D]
   void* slotV;
-  float* scK;           // int8 / fp8: [S+W][T][H]
+  float* scK;           // low-bit caches: [S+W][T][H] scales (fp32, or MX scale words)
   float* scV;
   int n_plan;
   int plan_slot[kMaxPlan];    // slot of frame i of the projected rows
