@@ -18,7 +18,7 @@ as a baseline.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--no-components] [--no-rollouts]
                     [--workload steady|rollout|long_int8|recache|sweep|append|steady_int8|steady_fp8|
-                                steady_mxfp4|steady_mxfp8]
+                                steady_mxfp4|steady_mxfp8|long_mxfp4|long_mxfp8]
 """
 
 import argparse
@@ -485,13 +485,15 @@ def run_recache_stack(torch, ll, synth, cfg):
     return res
 
 
-def run_rollout(torch, ll, synth, cfg):
+def run_rollout(torch, ll, synth, cfg, kv=None):
     """Whole multi-layer rollout: per chunk, `passes` attention calls per layer, then one
     append per layer (and the recache of every layer before chunks k*recache_every).
-    Inputs come from a pool of seeded device tensors made before timing."""
+    Inputs come from a pool of seeded device tensors made before timing.  kv: the cache
+    format (default: the workload's, int8 or bf16)."""
     C, T, H, D, S, W = cfg.chunk_frames, cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.sink, cfg.window
     shape = (cfg.nq, H, D)
-    kv = "int8" if cfg.kv_int8 else "bf16"
+    if kv is None:
+        kv = "int8" if cfg.kv_int8 else "bf16"
     cache = ll.Cache(cfg.layers, H, D, T, S, W, kv_dtype=kv)
     pool = [tuple(synth.normal_bf16_device(shape, cfg.sigma, cfg.seed, t, 2000 + i) for t in range(3))
             for i in range(POOL)]
@@ -531,7 +533,8 @@ def run_rollout(torch, ll, synth, cfg):
     gpu_s = e0.elapsed_time(e1) / 1e3
     frames = cfg.chunks * C
     cache.close()
-    return {"workload": cfg.name, "layers": cfg.layers, "kv": kv, "latent_frames": frames, "seconds": gpu_s,
+    name = cfg.name if kv == ("int8" if cfg.kv_int8 else "bf16") else f"{cfg.name}, {kv} cache"
+    return {"workload": name, "layers": cfg.layers, "kv": kv, "latent_frames": frames, "seconds": gpu_s,
             "wall_s": wall, "latent_frames_per_s_stack": frames / gpu_s,
             "latent_frames_per_s_per_layer": frames * cfg.layers / gpu_s, "attention_flop": flops,
             "append_bytes": app_bytes, "avg_tflops_incl_append": flops / gpu_s / 1e12,
@@ -702,7 +705,7 @@ def main():
                          "the components")
     ap.add_argument("--workload", default="steady",
                     choices=["steady", "rollout", "long_int8", "recache", "sweep", "append", "steady_int8",
-                             "steady_fp8", "steady_mxfp4", "steady_mxfp8"],
+                             "steady_fp8", "steady_mxfp4", "steady_mxfp8", "long_mxfp4", "long_mxfp8"],
                     help="steady (default): the one-chunk step below; the others print their own "
                          "JSON record: 30-layer rollout, 400-chunk int8 rollout with recache, "
                          "30-layer recache, window/sink sweep, appends only (warm and cold), the "
@@ -742,6 +745,8 @@ def main():
             rec = run_rollout(torch, ll, synth, configs.ROLLOUT)
         elif args.workload == "long_int8":
             rec = run_rollout(torch, ll, synth, configs.LONG_INT8)
+        elif args.workload in ("long_mxfp4", "long_mxfp8"):
+            rec = run_rollout(torch, ll, synth, configs.LONG_INT8, kv=args.workload.split("_")[1])
         elif args.workload == "recache":
             rec = run_recache_stack(torch, ll, synth, configs.RECACHE)
         elif args.workload == "append":
