@@ -2,7 +2,8 @@
 
 24 configurations drawn from a fixed seed: sink 0-4, window 0-10, shot sink 0-2 frames,
 16 / 48 / 96 tokens per frame, 1-3 heads, head_dim 64 or 128, chunks of 1-3 frames with
-ragged lengths, bf16 / int8 / fp8 caches.  Each runs 10 chunks with a shot start (when
+ragged lengths, bf16 / int8 / fp8 caches; and 12 more from another seed with MXFP4 / MXFP8
+caches.  Each runs 10 chunks with a shot start (when
 the cache has a shot sink), a full recache after chunk 5 and a window-only recache after
 chunk 7 (when the cache holds such frames).  Every attention output is compared with the
 oracle in full; the slot maps and bytes are compared after every recache and at the end.
@@ -22,7 +23,7 @@ from helpers import History, check_slots, compare_attention
 pytestmark = pytest.mark.gpu
 
 
-def _configs(n=24, seed=790):
+def _configs(n=24, seed=790, formats=("bf16", "int8", "fp8"), first=0):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
@@ -33,8 +34,8 @@ def _configs(n=24, seed=790):
         H = int(rng.integers(1, 4))
         D = int(rng.choice([64, 128]))
         C = int(rng.integers(1, 4))
-        kv = str(rng.choice(["bf16", "int8", "fp8"]))
-        out.append((len(out), S, W, Ss, T, H, D, C, kv))
+        kv = str(rng.choice(list(formats)))
+        out.append((first + len(out), S, W, Ss, T, H, D, C, kv))
     return out
 
 
@@ -47,7 +48,8 @@ def torch_gpu():
     return torch
 
 
-@pytest.mark.parametrize("cfg", _configs(), ids=lambda c: "i%d_S%d_W%d_Ss%d_T%d_H%d_D%d_C%d_%s" % c)
+@pytest.mark.parametrize("cfg", _configs() + _configs(12, 791, ("mxfp4", "mxfp8"), first=24),
+                         ids=lambda c: "i%d_S%d_W%d_Ss%d_T%d_H%d_D%d_C%d_%s" % c)
 def test_random_configuration(torch_gpu, cfg):
     i, S, W, Ss, T, H, D, C, kv = cfg
     rng = np.random.default_rng(800 + i)
